@@ -1,0 +1,384 @@
+"""Pins for the fp64 oracle: it is checked against things other than itself.
+
+Map of pins (function -> what fixes it):
+
+* oracle.attention: pure-Python brute force written from the definition
+  (no max shift, math.exp); the two-key logistic closed form; V = I gives
+  P with rows summing to 1; V = 1 gives 1; Q = 0 gives mean(V); one key
+  gives V; scipy.special.logsumexp for lse; joint key permutation and query
+  permutation equivariance; shift invariance at logits near 10^3 where a
+  softmax without the max shift overflows.
+* oracle.geometry / cube_layout: the numbers printed in "Anatomy of Wan2.2's
+  53.6x speedup", sections "VSA selects cubes" and "Roofline analysis set
+  the 3.35 ms target" (tests/golden/page4_vsa_480p.json); hand-computed
+  cube ids and slots; a per-token loop on a ragged grid.
+* oracle.pool / coarse_scores / select_topk / fine / vsa: a brute-force
+  VSA written with Python loops and sorted() on a ragged 5x6x7 grid; top-k
+  = all cubes reduces to dense attention; Q = 0 makes every score tie so the
+  plan is cubes 0..k-1 and O is the mean of their real V rows; permuting
+  tokens inside a key cube leaves everything unchanged; one-cube grids
+  reduce to dense; a hand-made score table for the tie rule and margins.
+* oracle.flops_fine / kv_stream_bytes: the page's 3.35 TFLOP and 64 GB.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+import oracle
+
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------- dense
+
+def brute_attention(q, k, v, scale):
+    """Softmax attention with Python loops and math.exp, straight from the definition."""
+    N, D = len(q), len(q[0])
+    M, Dv = len(k), len(v[0])
+    out, lses = [], []
+    for i in range(N):
+        w = []
+        for j in range(M):
+            s = 0.0
+            for d in range(D):
+                s += q[i][d] * k[j][d]
+            w.append(math.exp(scale * s))
+        tot = sum(w)
+        out.append([sum(w[j] * v[j][e] for j in range(M)) / tot for e in range(Dv)])
+        lses.append(math.log(tot))
+    return np.array(out), np.array(lses)
+
+
+@pytest.mark.parametrize("N,M,D,Dv", [(5, 7, 4, 3), (9, 13, 8, 8), (1, 1, 3, 2), (16, 3, 6, 5)])
+def test_dense_brute_force(N, M, D, Dv):
+    r = rng(N * 100 + M)
+    q, k, v = r.normal(size=(N, D)), r.normal(size=(M, D)), r.normal(size=(M, Dv))
+    scale = 1 / math.sqrt(D)
+    o, lse = oracle.attention(q, k, v, scale)
+    ob, lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), scale)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-12)
+
+
+def test_dense_two_keys_is_logistic():
+    r = rng(3)
+    q, k, v = r.normal(size=(4, 8)), r.normal(size=(2, 8)), r.normal(size=(2, 5))
+    s = 0.37
+    o, _ = oracle.attention(q, k, v, s)
+    for i in range(4):
+        a = s * (q[i] @ k[0] - q[i] @ k[1])
+        w0 = 1.0 / (1.0 + math.exp(-a))
+        np.testing.assert_allclose(o[i], w0 * v[0] + (1 - w0) * v[1], atol=1e-13)
+
+
+def test_dense_rows_sum_to_one_and_match_probabilities():
+    r = rng(4)
+    N, M, D = 11, 17, 8
+    q, k = r.normal(size=(N, D)) * 2, r.normal(size=(M, D)) * 2
+    P, _ = oracle.attention(q, k, np.eye(M), 0.5)          # V = I gives P itself
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
+    assert (P > 0).all()
+    Pb, _ = brute_attention(q.tolist(), k.tolist(), np.eye(M).tolist(), 0.5)
+    np.testing.assert_allclose(P, Pb, atol=1e-12)
+    ones, _ = oracle.attention(q, k, np.ones((M, 3)), 0.5)
+    np.testing.assert_allclose(ones, 1.0, atol=1e-12)
+
+
+def test_dense_closed_forms():
+    r = rng(5)
+    M, D = 23, 16
+    k, v = r.normal(size=(M, D)), r.normal(size=(M, 7))
+    o, lse = oracle.attention(np.zeros((3, D)), k, v, 0.25)
+    np.testing.assert_allclose(o, np.tile(v.mean(axis=0), (3, 1)), atol=1e-12)
+    np.testing.assert_allclose(lse, math.log(M), atol=1e-12)
+    o1, lse1 = oracle.attention(r.normal(size=(4, D)), k[:1], v[:1], 0.25)
+    np.testing.assert_allclose(o1, np.tile(v[0], (4, 1)), atol=1e-14)
+
+
+def test_dense_lse_matches_library_logsumexp():
+    r = rng(6)
+    q, k, v = r.normal(size=(40, 32)) * 3, r.normal(size=(300, 32)) * 3, r.normal(size=(300, 4))
+    s = 1 / math.sqrt(32)
+    _, lse = oracle.attention(q, k, v, s, chunk=7)
+    np.testing.assert_allclose(lse, logsumexp(s * q @ k.T, axis=1), rtol=1e-13)
+
+
+def test_dense_permutation_equivariance():
+    r = rng(7)
+    q, k, v = r.normal(size=(20, 8)), r.normal(size=(30, 8)), r.normal(size=(30, 6))
+    o, lse = oracle.attention(q, k, v, 0.4)
+    pk = r.permutation(30)
+    o2, lse2 = oracle.attention(q, k[pk], v[pk], 0.4)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, atol=1e-13)
+    pq = r.permutation(20)
+    o3, _ = oracle.attention(q[pq], k, v, 0.4)
+    np.testing.assert_allclose(o3, o[pq], atol=1e-13)
+    # swapping the roles of q and k is NOT a symmetry: catches a transposed operand
+    o4, _ = oracle.attention(k[:20], q, v[:20], 0.4)
+    assert not np.allclose(o4, o)
+
+
+def test_dense_shift_invariance_at_overflowing_logits():
+    """A common shift of every logit of a row changes nothing, even near 1e3.
+
+    Appending a column to q (value 1) and to k (value c/scale) adds c to every
+    logit.  Without subtracting the row maximum exp(1000) would overflow.
+    """
+    r = rng(8)
+    q, k, v = r.normal(size=(6, 8)), r.normal(size=(50, 8)), r.normal(size=(50, 3))
+    s = 0.5
+    o, lse = oracle.attention(q, k, v, s)
+    c = 1000.0
+    qa = np.hstack([q, np.ones((6, 1))])
+    ka = np.hstack([k, np.full((50, 1), c / s)])
+    oa, lsea = oracle.attention(qa, ka, v, s)
+    assert np.isfinite(oa).all()
+    with np.errstate(over="ignore", invalid="ignore"):
+        naive = np.exp(s * qa @ ka.T)
+        assert not np.isfinite((naive @ v) / naive.sum(1, keepdims=True)).all()
+    np.testing.assert_allclose(oa, o, atol=1e-12)
+    np.testing.assert_allclose(lsea, lse + c, rtol=1e-15)
+
+
+def test_dense_row_subset_and_heads():
+    r = rng(9)
+    q, k, v = r.normal(size=(2, 3, 50, 8)), r.normal(size=(2, 3, 50, 8)), r.normal(size=(2, 3, 50, 8))
+    rows = [0, 7, 49]
+    o, lse = oracle.attention_heads(q, k, v, 0.3, rows)
+    for b in range(2):
+        for h in range(3):
+            ob, lb = brute_attention(q[b, h, rows].tolist(), k[b, h].tolist(), v[b, h].tolist(), 0.3)
+            np.testing.assert_allclose(o[b, h], ob, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], lb, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- geometry
+
+@pytest.fixture(scope="module")
+def page4(golden_dir):
+    with open(os.path.join(golden_dir, "page4_vsa_480p.json")) as f:
+        return json.load(f)
+
+
+def test_geometry_matches_page(page4):
+    g = oracle.geometry(page4["T"], page4["H"], page4["W"])
+    assert g["N"] == page4["tokens"]
+    assert (g["Tp"], g["Hp"], g["Wp"]) == (page4["padded_T"], page4["padded_H"], page4["padded_W"])
+    assert g["Np"] == page4["padded_tokens"]
+    assert [g["nt"], g["nh"], g["nw"]] == page4["cube_grid"]
+    assert g["C"] == page4["cubes"]
+    assert g["C"] * page4["heads"] == page4["output_tiles"]
+    assert round(g["C"] * (1 - page4["sparsity"])) == page4["kept_cubes"]
+
+
+def test_cost_conventions_match_page(page4):
+    fl = oracle.flops_fine(page4["tokens"], page4["kept_cubes"], page4["head_dim"], page4["heads"])
+    assert round(fl / 1e12, 2) == page4["tflop_rounded"]
+    kv = oracle.kv_stream_bytes(page4["cubes"], page4["kept_cubes"], page4["head_dim"], page4["heads"])
+    assert round(kv / 1e9) == page4["kv_stream_gb_rounded"]
+
+
+def test_cube_layout_hand_values():
+    tok = oracle.cube_layout(21, 30, 52)
+    assert tok.shape == (624, 64)
+    # token (t,h,w) = (0,0,0): cube 0 slot 0
+    assert tok[0, 0] == 0
+    # (0,0,5): cube (0,0,1) = 1, slot (0*4+0)*4+1 = 1
+    assert tok[1, 1] == 5
+    # (20,29,51): cube (5,7,12) = (5*8+7)*13+12 = 623, slot (0*4+1)*4+3 = 7
+    assert tok[623, 7] == (20 * 30 + 29) * 52 + 51
+    # (5,6,7): cube (1,1,1) = (1*8+1)*13+1 = 118, slot (1*4+2)*4+3 = 27
+    assert tok[118, 27] == (5 * 30 + 6) * 52 + 7
+    # the last t-layer of cubes (t=20..23) holds only t=20: 16 real tokens per full (h,w) cube
+    assert (tok[5 * 104] >= 0).sum() == 16
+    # a corner cube (t 20-23, h 28-31, w 48-51): 1*2*4 = 8 real tokens, the minimum at 480p
+    assert (tok[623] >= 0).sum() == 8
+    # every real token appears exactly once
+    real = tok[tok >= 0]
+    assert np.array_equal(np.sort(real), np.arange(21 * 30 * 52))
+
+
+def test_cube_layout_against_token_loop():
+    T, H, W = 5, 6, 7
+    tok = oracle.cube_layout(T, H, W)
+    seen = {}
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                c = ((t // 4) * 2 + h // 4) * 2 + w // 4
+                s = ((t % 4) * 4 + h % 4) * 4 + w % 4
+                seen[(c, s)] = (t * H + h) * W + w
+    for c in range(8):
+        for s in range(64):
+            assert tok[c, s] == seen.get((c, s), -1)
+
+
+# --------------------------------------------------------------------------- VSA
+
+def brute_vsa(q, k, v, T, H, W, topk, scale):
+    """VSA with Python loops: membership by (t//4, h//4, w//4), sorted() for top-k."""
+    nt, nh, nw = -(-T // 4), -(-H // 4), -(-W // 4)
+    members = {}
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                c = ((t // 4) * nh + h // 4) * nw + w // 4
+                members.setdefault(c, []).append((t * H + h) * W + w)
+    C = nt * nh * nw
+    D = len(q[0])
+
+    def mean(x, rows):
+        return [sum(x[r][d] for r in rows) / len(rows) for d in range(D)]
+
+    qb = [mean(q, members[c]) for c in range(C)]
+    kb = [mean(k, members[c]) for c in range(C)]
+    scores = [[scale * sum(qb[c][d] * kb[c2][d] for d in range(D)) for c2 in range(C)] for c in range(C)]
+    idx = []
+    for c in range(C):
+        ranked = sorted(range(C), key=lambda c2: (-scores[c][c2], c2))
+        idx.append(sorted(ranked[:topk]))
+    o = [None] * (T * H * W)
+    for c in range(C):
+        keys = [j for c2 in idx[c] for j in members[c2]]
+        ob, _ = brute_attention([q[i] for i in members[c]], [k[j] for j in keys], [v[j] for j in keys], scale)
+        for a, i in enumerate(members[c]):
+            o[i] = ob[a]
+    return np.array(scores), np.array(idx), np.array(o)
+
+
+@pytest.mark.parametrize("topk", [1, 3, 8])
+def test_vsa_brute_force_ragged_grid(topk):
+    T, H, W, D = 5, 6, 7, 8
+    N = T * H * W
+    r = rng(10 + topk)
+    # a smooth field plus noise so cube scores differ clearly
+    pos = np.stack(np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij"), -1).reshape(N, 3)
+    f = np.cos(pos @ r.normal(size=(3, D)) * 0.6 + r.uniform(0, 6, D))
+    q, k, v = f * 2 + r.normal(size=(N, D)), f * 2 + r.normal(size=(N, D)), r.normal(size=(N, D))
+    s = 1 / math.sqrt(D)
+    res = oracle.vsa(q, k, v, T, H, W, topk, s)
+    sb, ib, ob = brute_vsa(q.tolist(), k.tolist(), v.tolist(), T, H, W, topk, s)
+    np.testing.assert_allclose(res["scores"], sb, atol=1e-12)
+    assert np.array_equal(res["idx"], ib)
+    np.testing.assert_allclose(res["o"], ob, atol=1e-12)
+
+
+def test_vsa_all_cubes_equals_dense():
+    T, H, W, D = 6, 9, 10, 16
+    N = T * H * W
+    r = rng(12)
+    q, k, v = r.normal(size=(N, D)), r.normal(size=(N, D)), r.normal(size=(N, D))
+    C = oracle.geometry(T, H, W)["C"]
+    res = oracle.vsa(q, k, v, T, H, W, C, 0.25)
+    od, ld = oracle.attention(q, k, v, 0.25)
+    np.testing.assert_allclose(res["o"], od, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], ld, atol=1e-12)
+    assert np.isinf(res["margin"]).all()
+
+
+def test_vsa_zero_queries_tie_to_first_cubes():
+    T, H, W, D, topk = 7, 5, 9, 8, 3
+    N = T * H * W
+    r = rng(13)
+    k, v = r.normal(size=(N, D)), r.normal(size=(N, D))
+    res = oracle.vsa(np.zeros((N, D)), k, v, T, H, W, topk, 0.3)
+    C = oracle.geometry(T, H, W)["C"]
+    assert np.array_equal(res["idx"], np.tile(np.arange(topk), (C, 1)))
+    tok = oracle.cube_layout(T, H, W)
+    sel = tok[:topk].ravel()
+    expect = v[sel[sel >= 0]].mean(axis=0)
+    np.testing.assert_allclose(res["o"], np.tile(expect, (N, 1)), atol=1e-12)
+
+
+def test_vsa_within_cube_permutation_invariance():
+    T, H, W, D, topk = 8, 8, 6, 8, 2
+    N = T * H * W
+    r = rng(14)
+    f = np.cos(np.arange(N)[:, None] * r.normal(size=(1, D)) * 0.05)
+    q, k, v = f * 3 + r.normal(size=(N, D)), f * 3 + r.normal(size=(N, D)), r.normal(size=(N, D))
+    base = oracle.vsa(q, k, v, T, H, W, topk, 0.35)
+    tok = oracle.cube_layout(T, H, W)
+    c = 5
+    members = tok[c][tok[c] >= 0]
+    perm = np.arange(N)
+    perm[members] = members[r.permutation(members.size)]
+    k2, v2 = k[perm], v[perm]
+    res = oracle.vsa(q, k2, v2, T, H, W, topk, 0.35)
+    np.testing.assert_allclose(res["kbar"], base["kbar"], atol=1e-13)
+    assert np.array_equal(res["idx"], base["idx"])
+    np.testing.assert_allclose(res["o"], base["o"], atol=1e-12)
+
+
+@pytest.mark.parametrize("grid", [(4, 4, 4), (3, 2, 3), (1, 1, 1)])
+def test_vsa_single_cube_is_dense(grid):
+    T, H, W = grid
+    N, D = T * H * W, 8
+    r = rng(N)
+    q, k, v = r.normal(size=(N, D)), r.normal(size=(N, D)), r.normal(size=(N, D))
+    res = oracle.vsa(q, k, v, T, H, W, 1, 0.5)
+    od, _ = oracle.attention(q, k, v, 0.5)
+    np.testing.assert_allclose(res["o"], od, atol=1e-12)
+    np.testing.assert_allclose(res["qbar"][0], q.mean(axis=0), atol=1e-14)
+
+
+def test_select_topk_tie_rule_and_margin():
+    scores = np.array([[3.0, 1.0, 3.0, 2.0],
+                       [0.0, 0.0, 0.0, 0.0],
+                       [-1.0, 5.0, 4.5, 5.0]])
+    idx, m = oracle.select_topk(scores, 2)
+    assert idx.tolist() == [[0, 2], [0, 1], [1, 3]]
+    np.testing.assert_allclose(m, [1.0, 0.0, 0.5])
+    idx3, m3 = oracle.select_topk(scores, 3)
+    assert idx3.tolist() == [[0, 2, 3], [0, 1, 2], [1, 2, 3]]
+    np.testing.assert_allclose(m3, [1.0, 0.0, 5.5])
+    with pytest.raises(ValueError):
+        oracle.select_topk(scores, 5)
+
+
+def test_pool_uses_real_tokens_only():
+    T, H, W, D = 5, 5, 5, 3
+    N = T * H * W
+    x = np.arange(N * D, dtype=np.float64).reshape(N, D)
+    tok = oracle.cube_layout(T, H, W)
+    qb = oracle.pool(x, tok)
+    # the far corner cube (t,h,w >= 4) holds only the token (4,4,4)
+    last = (4 * 5 + 4) * 5 + 4
+    np.testing.assert_allclose(qb[-1], x[last])
+    # cube (0,0,1) holds w = 4 only, for t,h < 4: 16 tokens
+    rows = [(t * 5 + h) * 5 + 4 for t in range(4) for h in range(4)]
+    np.testing.assert_allclose(qb[1], x[rows].mean(axis=0))
+
+
+def test_near_tie_tolerance_bounds_fp32_scores():
+    """fp32 cube means and fp32 dot products (any order) stay within tau/4 of fp64."""
+    T, H, W, D = 9, 10, 11, 128
+    N = T * H * W
+    r = rng(15)
+    q, k = (r.normal(size=(N, D)) * 2).astype(np.float32), (r.normal(size=(N, D)) * 2).astype(np.float32)
+    tok = oracle.cube_layout(T, H, W)
+    s = 1 / math.sqrt(D)
+    exact = oracle.coarse_scores(oracle.pool(q.astype(np.float64), tok), oracle.pool(k.astype(np.float64), tok), s)
+    tau = oracle.near_tie_tolerance(q.astype(np.float64), k.astype(np.float64), tok, s)
+    valid = tok >= 0
+
+    def pool32(x):
+        acc = np.zeros((tok.shape[0], D), np.float32)
+        for slot in range(64):                      # sequential fp32 sums
+            acc += np.where(valid[:, slot, None], x[np.maximum(tok[:, slot], 0)], np.float32(0))
+        return acc / valid.sum(axis=1)[:, None].astype(np.float32)
+
+    qb, kb = pool32(q), pool32(k)
+    s32 = np.zeros((qb.shape[0], kb.shape[0]), np.float32)
+    for d in range(D):                              # sequential fp32 dot products
+        s32 += qb[:, d:d + 1] * kb[None, :, d]
+    s32 *= np.float32(s)
+    err = np.abs(s32.astype(np.float64) - exact).max(axis=1)
+    assert (err <= tau / 4).all()
