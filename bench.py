@@ -1,0 +1,225 @@
+"""Benchmark: dense and VSA self-attention at the 480p Wan2.2 shape on one MI355X.
+
+One step = one pass of the whole hot path on synthetic inputs already resident
+in HBM:
+  * dense attention, CFG pair x 40 heads x 32,760 tokens x d128 (one call);
+  * VSA, 1 x 40 heads, grid 21x30x52 padded to 624 cubes, top-32: the coarse
+    call (gather + pool, scores, top-k) and the fine call.
+Prints one JSON line.  The per-kernel times come from HIP events the library
+records on the launch stream around each kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+DENSE = "dense_480p_cfg"
+VSA = "vsa_480p"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (used for profiler runs)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def git_rev() -> str:
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                              text=True, timeout=10).stdout.strip() or "unknown"
+    except Exception:
+        return "unknown"
+
+
+def dense_flops(wl) -> float:
+    return 4.0 * wl.B * wl.Hh * wl.N * wl.N * wl.D
+
+
+def vsa_flops(wl, C) -> dict:
+    fine = 4.0 * wl.B * wl.Hh * wl.N * 64 * wl.topk * wl.D        # padded queries excluded
+    coarse = 2.0 * wl.B * wl.Hh * C * C * wl.D
+    return dict(fine=fine, coarse=coarse, total=fine + coarse)
+
+
+def vsa_bytes(wl, C) -> dict:
+    Np = 64 * C
+    BH = wl.B * wl.Hh
+    gather = BH * (3 * wl.N * wl.D * 2 + 3 * Np * wl.D * 2 + 2 * C * wl.D * 4)
+    scores = BH * (2 * C * wl.D * 4 + C * C * 4)
+    topk = BH * (C * C * 4 + C * wl.topk * 4)
+    return dict(gather=gather, scores=scores, topk=topk)
+
+
+def cpu_baseline(seconds: float) -> dict:
+    """The fp64 oracle on a bounded sample of the dense workload: query rows of one head."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = os.cpu_count() or 1
+    wl = synth.WORKLOADS[DENSE]
+    q = synth.bits_to_f64(synth.make_slice(wl, "q", 0, 0))
+    k = synth.bits_to_f64(synth.make_slice(wl, "k", 0, 0))
+    v = synth.bits_to_f64(synth.make_slice(wl, "v", 0, 0))
+    rows = 256
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, wl.scale, rows=np.arange(rows))
+    probe = time.perf_counter() - t0
+    rows = int(min(wl.N, max(256, rows * (seconds / max(probe, 1e-3)))))
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, wl.scale, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    flops = 4.0 * rows * wl.N * wl.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, dense attention of {rows} query rows x {wl.N} keys x d{wl.D} "
+                      f"of head (0,0) of the {DENSE} workload ({dt:.1f} s); "
+                      f"ms per full dense call extrapolated: {dt * 1e3 * wl.B * wl.Hh * wl.N / rows:.0f}",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import video_diffusion_dit_amd as wf
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wd, wv = synth.WORKLOADS[DENSE], synth.WORKLOADS[VSA]
+    qd, kd, vd = (to_dev(x) for x in synth.make_qkv(wd))
+    qv, kv, vv = (to_dev(x) for x in synth.make_qkv(wv))
+    C = wf.num_cubes(wv.T, wv.H, wv.W)
+    od = torch.empty((wd.B, wd.Hh, wd.N, wd.D), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(wf.dense_workspace_bytes(wd.B, wd.Hh, wd.N, wd.D), dtype=torch.uint8, device=dev)
+    ov = torch.empty((wv.B, wv.Hh, wv.N, wv.D), dtype=torch.float32, device=dev)
+    idx = torch.empty((wv.B, wv.Hh, C, wv.topk), dtype=torch.int32, device=dev)
+    ws_v = torch.empty(wf.vsa_workspace_bytes(wv.B, wv.Hh, wv.T, wv.H, wv.W, wv.D), dtype=torch.uint8,
+                       device=dev)
+    grid = (wv.T, wv.H, wv.W)
+
+    def step():
+        wf.wf_attn_dense(qd, kd, vd, out=od, workspace=ws_d)
+        wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
+        wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wf.profile_enable(True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    kern = {}
+    for name in ("wf_transpose_v", "wf_dense_fwd", "wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk",
+                 "wf_vsa_fine"):
+        n, tot = wf.profile_query(name)
+        kern[name] = tot / n
+    wf.profile_enable(False)
+
+    fl_d = dense_flops(wd)
+    fl_v = vsa_flops(wv, C)
+    by_v = vsa_bytes(wv, C)
+    ms_dense = kern["wf_transpose_v"] + kern["wf_dense_fwd"]
+    ms_vsa = kern["wf_vsa_gather"] + kern["wf_vsa_scores"] + kern["wf_vsa_topk"] + kern["wf_vsa_fine"]
+    dense_tf = fl_d / (kern["wf_dense_fwd"] * 1e-3) / 1e12
+    # dense attention at the VSA call's own shape (B=1, 40 heads) is half the CFG-pair call
+    ms_dense_same = ms_dense * wv.B / wd.B
+    out = {
+        "metric": "attention TFLOP/s and ms/call at 32,760 tok x 40 heads x d128 (dense, VSA)",
+        "value": (fl_d + fl_v["total"]) / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense MHA 2x40x32760xd128 (CFG pair, grid 21x30x52) + VSA 1x40 heads, "
+                        "grid 21x30x52 -> 24x32x52, 624 cubes, top-32",
+            "dense": {"B": wd.B, "heads": wd.Hh, "tokens": wd.N, "head_dim": wd.D},
+            "vsa": {"B": wv.B, "heads": wv.Hh, "tokens": wv.N, "cubes": C, "topk": wv.topk,
+                    "head_dim": wv.D},
+            "inputs": "bf16 N(0,1) + 2*phi(t,h,w), seeded random Fourier features",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "wf_dense_fwd",
+            "achieved": dense_tf,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": dense_tf / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+        "dense": {
+            "ms_per_call": ms_dense,
+            "kernel_ms": {"wf_transpose_v": kern["wf_transpose_v"], "wf_dense_fwd": kern["wf_dense_fwd"]},
+            "tflops_call": fl_d / (ms_dense * 1e-3) / 1e12,
+            "tflops_kernel": dense_tf,
+            "frac_bf16_peak": dense_tf / PEAK_BF16_TFLOPS,
+            "algorithmic_tflop": fl_d / 1e12,
+        },
+        "vsa": {
+            "ms_per_call": ms_vsa,
+            "kernel_ms": {k: kern[k] for k in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine")},
+            "fine_tflops": fl_v["fine"] / (kern["wf_vsa_fine"] * 1e-3) / 1e12,
+            "fine_frac_bf16_peak": fl_v["fine"] / (kern["wf_vsa_fine"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "gather_gbs": by_v["gather"] / (kern["wf_vsa_gather"] * 1e-3) / 1e9,
+            "topk_gbs": by_v["topk"] / (kern["wf_vsa_topk"] * 1e-3) / 1e9,
+            "scores_gbs": by_v["scores"] / (kern["wf_vsa_scores"] * 1e-3) / 1e9,
+            "dense_equivalent_speedup": ms_dense_same / ms_vsa,
+            "dense_equivalent_tflops": fl_d * wv.B / wd.B / (ms_vsa * 1e-3) / 1e12,
+            "ideal_speedup": C / wv.topk,
+        },
+        "context": {"pages_dense_ms_b200": 17.0,
+                    "our_dense_ms_one_cfg_branch": ms_dense_same},
+        "wall_s_timed_region": wall,
+        "device": torch.cuda.get_device_name(dev),
+        "git": git_rev(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * wf_attn.h -- C ABI of libwfattn.so: multi-head self-attention over a video
+ * diffusion transformer's 3D latent token grid on AMD Instinct MI355X (gfx950).
+ *
+ * Two forms of the same operation, as described in "Anatomy of Wan2.2's 53.6x
+ * speedup" (zharfai.com, review of Baseten's Wan2.2 work):
+ *
+ *   - dense attention, section "Why video attention becomes the bottleneck":
+ *     every query token of the T x H x W grid against every key token,
+ *     O = softmax(scale * Q K^T) V per (batch, head), no mask;
+ *   - Video Sparse Attention (VSA), section "VSA selects cubes": the grid is
+ *     padded to multiples of 4 and cut into 4x4x4 cubes of 64 tokens; a coarse
+ *     stage scores cube-mean queries against cube-mean keys and keeps the
+ *     top-k key cubes of every query cube; a fine stage runs token-level
+ *     attention of each query cube over its kept cubes only.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Tensors are [B][Hh][N][D] row-major and contiguous, tokens in row-major
+ *   (t, h, w) order: n = (t*H + h)*W + w.  q, k, v are bfloat16 (passed as raw
+ *   pointers to 2-byte elements), outputs are float32.  Every pointer is a
+ *   device pointer (hipMalloc'd or equivalent) aligned to 16 bytes.
+ *   D (head dimension) is 64 or 128 for dense attention and 128 for VSA.
+ *
+ *   Ownership: the caller allocates and frees every buffer, workspaces
+ *   included.  The library never allocates or frees device memory and never
+ *   synchronises the stream (the opt-in WF_VALIDATE=1 index check in
+ *   wf_vsa_fine is the only exception, and it says so).  Work is enqueued on
+ *   `stream` (a hipStream_t; NULL means the null stream) in call order.
+ *   Calls are reentrant; concurrent calls must use distinct workspaces.
+ *
+ *   Errors: every entry point returns a wf_status.  Argument checks run on
+ *   the host before anything is enqueued; on failure nothing is enqueued and
+ *   wf_last_error_detail() (thread-local) says which argument was rejected.
+ *   WF_ERR_HIP reports a launch error from the HIP runtime.  There is no
+ *   fallback path: unsupported input is rejected, never rerouted.
+ */
+#ifndef WF_ATTN_H
+#define WF_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wf_status {
+  WF_OK = 0,
+  WF_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, bad size, non-finite scale */
+  WF_ERR_UNSUPPORTED = 2,  /* a head dimension or size this build does not handle */
+  WF_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes query */
+  WF_ERR_BAD_INDEX = 4,    /* a top-k plan that is out of range or not strictly ascending */
+  WF_ERR_HIP = 5           /* the HIP runtime reported an error */
+} wf_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* wf_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* wf_last_error_detail(void);
+
+/* ABI version of this library; bumped on any signature change. */
+int32_t wf_abi_version(void);
+
+/* ------------------------------------------------------------------ dense */
+
+/* Workspace bytes wf_attn_dense needs for these sizes (0 on invalid sizes). */
+size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D);
+
+/*
+ * Dense bidirectional attention ("Why video attention becomes the
+ * bottleneck"; the Wan2.1 blog, bafh001.com, section 4.2, calls it
+ * non-causally with QK^T, softmax and PV fused on chip).  Per (b, h):
+ *     o[i]   = sum_j softmax_j(scale * q[i] . k[j]) v[j]
+ *     lse[i] = log sum_j exp(scale * q[i] . k[j])          (natural log)
+ *
+ *   q, k, v    bf16 [B][Hh][N][D], read only.
+ *   o          fp32 [B][Hh][N][D], written.
+ *   lse        fp32 [B][Hh][N], written; may be NULL.
+ *   N          tokens (T*H*W), 1 <= N < 2^31 / D.
+ *   D          64 or 128.
+ *   scale      finite and > 0 (1/sqrt(D) for the standard operation).
+ *   workspace  device scratch of at least wf_attn_dense_workspace_bytes(),
+ *              16-byte aligned; contents on entry are ignored and the call
+ *              leaves it holding V transposed per head.
+ * The softmax keeps a running row maximum (section "Fixed-max softmax is a
+ * numerical contract" of the Wan2.2 review), so any finite input yields
+ * finite output.
+ */
+int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, float* lse,
+                      int32_t B, int32_t Hh, int32_t N, int32_t D, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------------- VSA */
+
+/* Number of 4x4x4 cubes of a T x H x W grid after padding each side up to a
+ * multiple of 4 ("VSA selects cubes": 21x30x52 gives 6x8x13 = 624); 0 if invalid. */
+int32_t wf_vsa_num_cubes(int32_t T, int32_t H, int32_t W);
+
+/* Workspace bytes that wf_vsa_coarse_topk fills and wf_vsa_fine reads
+ * (cube-ordered Q, K and V, cube-mean Q and K, coarse scores). 0 if invalid. */
+size_t wf_vsa_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D);
+
+/*
+ * VSA coarse stage ("VSA selects cubes", part 1).  With C = wf_vsa_num_cubes():
+ *   1. gathers q, k, v into cube order inside `workspace` (padded slots zero);
+ *   2. pools cube means Qbar, Kbar over each cube's real tokens, in fp32;
+ *   3. scores S[c][c'] = scale * Qbar[c] . Kbar[c'] in fp32;
+ *   4. writes idx[b][h][c][0..topk) = the topk key cubes c' with the largest
+ *      S[c][c'], equal scores resolved toward the smaller c', listed in
+ *      strictly ascending order.
+ * Cube c of the padded grid is (ct*nh + ch)*nw + cw with cube coordinates
+ * (ct, ch, cw) = (t/4, h/4, w/4).
+ *
+ *   q, k, v        bf16 [B][Hh][T*H*W][D], read only.
+ *   T, H, W        real grid, each >= 1; D must be 128.
+ *   topk           1 <= topk <= C.
+ *   idx            int32 [B][Hh][C][topk], written.
+ *   coarse_scores  fp32 [B][Hh][C][C], written; may be NULL.
+ *   workspace      at least wf_vsa_workspace_bytes(); keep it untouched
+ *                  between this call and wf_vsa_fine.
+ */
+int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v,
+                           int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                           float scale, int32_t topk, int32_t* idx, float* coarse_scores,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * VSA fine stage ("VSA selects cubes", part 2): each real query token of cube
+ * c attends over the real key tokens of cubes idx[b][h][c][0..topk):
+ *     o[i]   = sum_{j in J(c)} softmax_j(scale * q[i] . k[j]) v[j]
+ *     lse[i] = log sum_{j in J(c)} exp(scale * q[i] . k[j])
+ * Padded key slots are masked out; padded query slots are not written.
+ *
+ *   workspace      as filled by wf_vsa_coarse_topk with the same B, Hh, T, H, W, D.
+ *   idx            int32 [B][Hh][C][topk]: any plan (the coarse stage's or the
+ *                  caller's) with entries in [0, C) strictly ascending per row.
+ *                  The kernels trust it unless the environment variable
+ *                  WF_VALIDATE=1 is set, in which case a check kernel runs
+ *                  first and the call synchronises `stream` to return
+ *                  WF_ERR_BAD_INDEX on a bad plan (nothing else enqueued).
+ *   o              fp32 [B][Hh][T*H*W][D] in grid order, written.
+ *   lse            fp32 [B][Hh][T*H*W], written; may be NULL.
+ */
+int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t* idx,
+                    int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                    float scale, int32_t topk, float* o, float* lse, void* stream);
+
+/* ------------------------------------------------------ per-kernel timing */
+
+/*
+ * Optional timing of every kernel this library launches, with HIP events
+ * recorded on the launch stream just before and after each kernel.
+ * wf_profile_enable(1) clears earlier records and starts recording;
+ * wf_profile_enable(0) stops.  Recording adds no synchronisation.
+ * At most 65536 launches are recorded per enable; later ones are counted
+ * as dropped and not timed.
+ */
+int32_t wf_profile_enable(int32_t on);
+
+/*
+ * Waits for the recorded events, then reports the kernel named `name`
+ * (e.g. "wf_dense_fwd"): number of timed launches and their summed time.
+ * Returns WF_ERR_INVALID_ARG if no launch of that kernel was recorded.
+ */
+int32_t wf_profile_query(const char* name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WF_ATTN_H */

@@ -93,14 +93,14 @@ def select_topk(scores: np.ndarray, k: int):
     C, Ck = scores.shape
     if not 1 <= k <= Ck:
         raise ValueError(f"top-k {k} outside [1, {Ck}]")
-    cols = np.arange(Ck)
-    idx = np.empty((C, k), dtype=np.int64)
+    # a stable sort of the negated scores: descending score, equal scores by ascending index
+    order = np.argsort(-scores, axis=1, kind="stable")
+    idx = np.sort(order[:, :k], axis=1)
     margin = np.full(C, np.inf)
-    for c in range(C):
-        order = np.lexsort((cols, -scores[c]))   # by score descending, then index ascending
-        idx[c] = np.sort(order[:k])
-        if k < Ck:
-            margin[c] = scores[c, order[k - 1]] - scores[c, order[k]]
+    if k < Ck:
+        kth = np.take_along_axis(scores, order[:, k - 1:k], axis=1)[:, 0]
+        nxt = np.take_along_axis(scores, order[:, k:k + 1], axis=1)[:, 0]
+        margin = kth - nxt
     return idx, margin
 
 

@@ -1,0 +1,210 @@
+"""VSA on the GPU (through the C ABI) against the fp64 oracle.
+
+Checks the selected key-cube indices (exactly, under the near-tie rule), the
+fine-stage output (the GPU's whole pipeline, and the fine stage alone on the
+GPU's own plan), the closed forms (Q = 0 ties, top-k = all cubes equals
+dense attention) and the error paths.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from wf_testutil import (LSE_MAX_ABS, assert_close, check_topk_rows, errors, log, pmap,
+                         to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wf():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import video_diffusion_dit_amd as wf
+    return wf
+
+
+def gpu_vsa(wf, wl, q, k, v, topk=None):
+    import torch
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    idx, scores, ws = wf.wf_vsa_coarse_topk(qd, kd, vd, (wl.T, wl.H, wl.W), topk or wl.topk,
+                                            with_scores=True)
+    o, lse = wf.wf_vsa_fine(ws, idx, tuple(qd.shape), (wl.T, wl.H, wl.W), with_lse=True)
+    torch.cuda.synchronize()
+    return dict(idx=idx.cpu().numpy(), scores=scores.cpu().numpy(), o=o.cpu().numpy(),
+                lse=lse.cpu().numpy(), ws=ws, idx_dev=idx)
+
+
+def coarse_ref(wl, q, k, heads, topk):
+    tok = oracle.cube_layout(wl.T, wl.H, wl.W)
+
+    def one(bh):
+        b, h = bh
+        qf, kf = synth.bits_to_f64(q[b, h]), synth.bits_to_f64(k[b, h])
+        qb, kb = oracle.pool(qf, tok), oracle.pool(kf, tok)
+        sc = oracle.coarse_scores(qb, kb, wl.scale)
+        idx, margin = oracle.select_topk(sc, topk)
+        return dict(scores=sc, idx=idx, margin=margin,
+                    tau=oracle.near_tie_tolerance(qf, kf, tok, wl.scale))
+    return dict(zip(heads, pmap(one, heads))), tok
+
+
+def check_scores_and_idx(g, ref, heads):
+    near = 0
+    for bh in heads:
+        r = ref[bh]
+        # fp32 scores within the tolerance the top-k rule assumes
+        assert np.abs(g["scores"][bh] - r["scores"]).max(axis=1).max() <= r["tau"].max() / 4
+        near += check_topk_rows(g["idx"][bh], r["scores"], r["idx"], r["margin"], r["tau"])
+    print(f"  near-tie rows: {near} of {len(heads) * g['idx'].shape[2]}", flush=True)
+    return near
+
+
+def check_fine(wl, q, k, v, g, tok, heads, cubes=None, topk=None):
+    def one(bh):
+        b, h = bh
+        return oracle.fine(synth.bits_to_f64(q[b, h]), synth.bits_to_f64(k[b, h]),
+                           synth.bits_to_f64(v[b, h]), tok, g["idx"][bh], wl.scale, cubes)
+    res = pmap(one, heads)
+    for bh, (o_ref, l_ref) in zip(heads, res):
+        m = ~np.isnan(l_ref)
+        assert_close(g["o"][bh][m], o_ref[m], f"fine O b{bh[0]} h{bh[1]} ({m.sum()} rows)")
+        assert errors(g["lse"][bh][m], l_ref[m])[0] <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("grid,topk,B,Hh", [((5, 6, 7), 1, 1, 2), ((5, 6, 7), 3, 2, 1),
+                                            ((5, 6, 7), 8, 1, 1), ((9, 10, 11), 5, 1, 2),
+                                            ((4, 4, 4), 1, 1, 1), ((1, 1, 1), 1, 1, 1),
+                                            ((13, 6, 21), 17, 1, 2)])
+def test_vsa_small_grids_all_outputs(wf, grid, topk, B, Hh):
+    T, H, W = grid
+    wl = synth.small_workload("vsa_small", B, Hh, T, H, W, 128, structured=True, seed=T * 100 + topk,
+                              topk=topk)
+    log(f"vsa small grid={grid} topk={topk} B={B} Hh={Hh}")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    heads = [(b, h) for b in range(B) for h in range(Hh)]
+    ref, tok = coarse_ref(wl, q, k, heads, topk)
+    check_scores_and_idx(g, ref, heads)
+    check_fine(wl, q, k, v, g, tok, heads)
+
+
+def test_vsa_all_cubes_equals_dense(wf):
+    wl = synth.small_workload("vsa_all", 1, 2, 7, 9, 10, 128, structured=True, seed=21)
+    C = wf.num_cubes(wl.T, wl.H, wl.W)
+    log(f"vsa topk=C={C} vs dense, grid 7x9x10")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v, topk=C)
+    assert (g["idx"] == np.arange(C)).all()
+    import torch
+    od, _ = wf.wf_attn_dense(to_device(q), to_device(k), to_device(v))
+    od = od.cpu().numpy()
+    for h in range(2):
+        ref, _ = oracle.attention(synth.bits_to_f64(q[0, h]), synth.bits_to_f64(k[0, h]),
+                                  synth.bits_to_f64(v[0, h]), wl.scale)
+        assert_close(g["o"][0, h], ref, f"VSA(k=C) h{h} vs oracle dense")
+        assert_close(g["o"][0, h], od[0, h], f"VSA(k=C) h{h} vs GPU dense", max_abs=1e-2, mean_abs=1e-3)
+
+
+def test_vsa_zero_queries_tie_rule(wf):
+    wl = synth.small_workload("vsa_q0", 1, 1, 8, 12, 9, 128, structured=True, seed=22, topk=4)
+    log("vsa Q=0 ties grid 8x12x9 topk=4")
+    q, k, v = synth.make_qkv(wl)
+    q[:] = 0
+    g = gpu_vsa(wf, wl, q, k, v)
+    C = g["idx"].shape[2]
+    assert (g["idx"][0, 0] == np.arange(4)).all(), "equal scores must resolve to the smallest cubes"
+    tok = oracle.cube_layout(wl.T, wl.H, wl.W)
+    sel = tok[:4].ravel()
+    expect = synth.bits_to_f64(v[0, 0])[sel[sel >= 0]].mean(axis=0)
+    assert_close(g["o"][0, 0], np.broadcast_to(expect, g["o"][0, 0].shape), "Q=0 O", max_abs=2e-3,
+                 mean_abs=5e-4)
+    assert C == 2 * 3 * 3
+
+
+def test_vsa_480p_full(wf):
+    wl = synth.WORKLOADS["vsa_480p"]
+    log(f"vsa {wl.name} B={wl.B} Hh={wl.Hh} grid {wl.T}x{wl.H}x{wl.W} topk={wl.topk} (all heads idx)")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    heads = [(0, h) for h in range(wl.Hh)]
+    ref, tok = coarse_ref(wl, q, k, heads, wl.topk)
+    check_scores_and_idx(g, ref, heads)
+    assert np.isfinite(g["o"]).all()
+    C = tok.shape[0]
+    cubes = sorted(set([0, 1, 12, 13, 103, 104, 311, 520, 622, 623] +
+                       np.random.default_rng(4).choice(C, 24, replace=False).tolist()))
+    check_fine(wl, q, k, v, g, tok, [(0, 0), (0, 17)], cubes)
+    check_fine(wl, q, k, v, g, tok, [(0, 39)])
+
+
+def test_vsa_720p_full(wf):
+    wl = synth.WORKLOADS["vsa_720p"]
+    log(f"vsa {wl.name} B={wl.B} Hh={wl.Hh} grid {wl.T}x{wl.H}x{wl.W} topk={wl.topk} (all heads idx)")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.Hh)]
+    ref, tok = coarse_ref(wl, q, k, heads, wl.topk)
+    check_scores_and_idx(g, ref, heads)
+    assert np.isfinite(g["o"]).all()
+    C = tok.shape[0]
+    cubes = sorted(set([0, 19, 20, 239, 240, 719, 1200, 1439] +
+                       np.random.default_rng(5).choice(C, 16, replace=False).tolist()))
+    check_fine(wl, q, k, v, g, tok, [(0, 3), (1, 36)], cubes)
+
+
+def test_vsa_fine_caller_plan_and_validation(wf, monkeypatch):
+    """A caller-supplied plan runs as given; with WF_VALIDATE=1 a bad plan is refused."""
+    import torch
+    wl = synth.small_workload("vsa_plan", 1, 2, 9, 10, 11, 128, structured=True, seed=23, topk=3)
+    log("vsa caller plan + validation grid 9x10x11")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    C = g["idx"].shape[2]
+    rng = np.random.default_rng(0)
+    plan = np.sort(np.stack([np.stack([rng.choice(C, 3, replace=False) for _ in range(C)])
+                             for _ in range(2)])[None], axis=-1).astype(np.int32)
+    plan_d = torch.from_numpy(plan).cuda()
+    shape = (1, 2, wl.N, 128)
+    monkeypatch.setenv("WF_VALIDATE", "1")
+    o, lse = wf.wf_vsa_fine(g["ws"], plan_d, shape, (wl.T, wl.H, wl.W), with_lse=True)
+    o = o.cpu().numpy()
+    tok = oracle.cube_layout(wl.T, wl.H, wl.W)
+    for h in range(2):
+        ref, _ = oracle.fine(synth.bits_to_f64(q[0, h]), synth.bits_to_f64(k[0, h]),
+                             synth.bits_to_f64(v[0, h]), tok, plan[0, h], wl.scale)
+        assert_close(o[0, h], ref, f"caller plan h{h}")
+    for bad in ("dup", "range", "order"):
+        p = plan.copy()
+        if bad == "dup":
+            p[0, 1, 5, 1] = p[0, 1, 5, 0]
+        elif bad == "range":
+            p[0, 0, 2, 2] = C
+        else:
+            p[0, 0, 7] = p[0, 0, 7][::-1]
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_vsa_fine(g["ws"], torch.from_numpy(p).cuda(), shape, (wl.T, wl.H, wl.W))
+        assert e.value.status == 4
+    monkeypatch.delenv("WF_VALIDATE")
+
+
+def test_vsa_error_paths(wf):
+    import torch
+    wl = synth.small_workload("vsa_err", 1, 1, 5, 6, 7, 128, seed=24)
+    q, k, v = synth.make_qkv(wl)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    for topk in (0, 9):
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_vsa_coarse_topk(qd, kd, vd, (5, 6, 7), topk)
+        assert e.value.status == 1
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_vsa_coarse_topk(qd, kd, vd, (5, 6, 7), 2, workspace=torch.empty(64, dtype=torch.uint8,
+                                                                                device="cuda"))
+    assert e.value.status == 3
+    q64 = to_device(q[..., :64].copy())
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_vsa_coarse_topk(q64, q64, q64, (5, 6, 7), 2)
+    assert e.value.status == 2

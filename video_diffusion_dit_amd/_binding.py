@@ -1,0 +1,184 @@
+"""ctypes binding of libwfattn.so (declarations in include/wf_attn.h).
+
+Argument marshalling only: every step of the computation runs in the
+library's HIP kernels.  PyTorch supplies device memory (outputs, workspaces)
+and the current HIP stream.  There is no fallback: if the library is not
+built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwfattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m video_diffusion_dit_amd.build` "
+                      "(or __graft_entry__.build()); there is no other implementation to fall back to")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_SIGS = {
+    "wf_status_string": (ctypes.c_char_p, [_i32]),
+    "wf_last_error_detail": (ctypes.c_char_p, []),
+    "wf_abi_version": (_i32, []),
+    "wf_attn_dense_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "wf_attn_dense": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "wf_vsa_num_cubes": (_i32, [_i32, _i32, _i32]),
+    "wf_vsa_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "wf_vsa_coarse_topk": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                  _vp, _vp, _vp, _sz, _vp]),
+    "wf_vsa_fine": (_i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp]),
+    "wf_profile_enable": (_i32, [_i32]),
+    "wf_profile_query": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
+                                ctypes.POINTER(ctypes.c_double)]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype, _fn.argtypes = _res, _args
+
+WF_OK, WF_ERR_INVALID_ARG, WF_ERR_UNSUPPORTED, WF_ERR_WORKSPACE, WF_ERR_BAD_INDEX, WF_ERR_HIP = range(6)
+
+
+class WfError(RuntimeError):
+    """A non-zero wf_status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = lib.wf_status_string(status).decode()
+        detail = lib.wf_last_error_detail().decode()
+        super().__init__(f"{where}: {name}: {detail}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != WF_OK:
+        raise WfError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _qkv_check(q, k, v):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 CUDA tensor [B, Hh, N, D]")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+
+
+def num_cubes(T: int, H: int, W: int) -> int:
+    return lib.wf_vsa_num_cubes(T, H, W)
+
+
+def dense_workspace_bytes(B: int, Hh: int, N: int, D: int) -> int:
+    return lib.wf_attn_dense_workspace_bytes(B, Hh, N, D)
+
+
+def vsa_workspace_bytes(B: int, Hh: int, T: int, H: int, W: int, D: int) -> int:
+    return lib.wf_vsa_workspace_bytes(B, Hh, T, H, W, D)
+
+
+def _workspace(nbytes: int, device, given=None):
+    torch = _torch()
+    if given is not None:
+        return given
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def wf_attn_dense(q, k, v, scale: Optional[float] = None, with_lse: bool = False,
+                  out=None, lse=None, workspace=None):
+    """Dense attention through wf_attn_dense.  Returns (o fp32 [B,Hh,N,D], lse or None)."""
+    torch = _torch()
+    _qkv_check(q, k, v)
+    B, Hh, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    ws = _workspace(dense_workspace_bytes(B, Hh, N, D), q.device, workspace)
+    _check(lib.wf_attn_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
+                             B, Hh, N, D, scale, ws.data_ptr(), ws.numel() * ws.element_size(),
+                             _stream_handle(q.device)), "wf_attn_dense")
+    return out, lse
+
+
+def wf_vsa_coarse_topk(q, k, v, grid, topk: int, scale: Optional[float] = None,
+                       with_scores: bool = False, idx=None, scores=None, workspace=None):
+    """VSA coarse stage through wf_vsa_coarse_topk.
+
+    grid = (T, H, W).  Returns (idx int32 [B,Hh,C,topk], scores or None,
+    workspace) -- pass the workspace on to wf_vsa_fine.
+    """
+    torch = _torch()
+    _qkv_check(q, k, v)
+    T, H, W = grid
+    B, Hh, N, D = q.shape
+    if N != T * H * W:
+        raise ValueError(f"N = {N} but the grid has {T * H * W} tokens")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    C = num_cubes(T, H, W)
+    if idx is None:
+        idx = torch.empty((B, Hh, C, max(topk, 1)), dtype=torch.int32, device=q.device)
+    if with_scores and scores is None:
+        scores = torch.empty((B, Hh, C, C), dtype=torch.float32, device=q.device)
+    ws = _workspace(vsa_workspace_bytes(B, Hh, T, H, W, D), q.device, workspace)
+    _check(lib.wf_vsa_coarse_topk(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D, scale,
+                                  topk, idx.data_ptr(), _ptr(scores), ws.data_ptr(),
+                                  ws.numel() * ws.element_size(), _stream_handle(q.device)),
+           "wf_vsa_coarse_topk")
+    return idx, scores, ws
+
+
+def wf_vsa_fine(workspace, idx, shape, grid, scale: Optional[float] = None, with_lse: bool = False,
+                out=None, lse=None):
+    """VSA fine stage through wf_vsa_fine.  shape = (B, Hh, N, D).  Returns (o, lse or None)."""
+    torch = _torch()
+    B, Hh, N, D = shape
+    T, H, W = grid
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 4:
+        raise ValueError("idx must be a contiguous int32 tensor [B, Hh, C, topk]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=idx.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, N), dtype=torch.float32, device=idx.device)
+    _check(lib.wf_vsa_fine(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           idx.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3], out.data_ptr(),
+                           _ptr(lse), _stream_handle(idx.device)), "wf_vsa_fine")
+    return out, lse
+
+
+def vsa(q, k, v, grid, topk: int, scale: Optional[float] = None, with_lse: bool = False,
+        with_scores: bool = False):
+    """Both VSA stages.  Returns dict(idx, o, lse, scores)."""
+    idx, scores, ws = wf_vsa_coarse_topk(q, k, v, grid, topk, scale, with_scores)
+    o, lse = wf_vsa_fine(ws, idx, tuple(q.shape), grid, scale, with_lse)
+    return dict(idx=idx, o=o, lse=lse, scores=scores)
+
+
+def profile_enable(on: bool) -> None:
+    _check(lib.wf_profile_enable(1 if on else 0), "wf_profile_enable")
+
+
+def profile_query(name: str):
+    """(launches, total_ms) of the kernel `name` since profile_enable(True)."""
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(lib.wf_profile_query(name.encode(), ctypes.byref(n), ctypes.byref(ms)), "wf_profile_query")
+    return n.value, ms.value

@@ -1,0 +1,271 @@
+// C ABI of libwfattn.so: argument validation, status codes, dispatch, and the
+// optional per-kernel event timing.  Declarations and contracts: wf_attn.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "wf_attn.h"
+#include "wf_launch.hpp"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int32_t fail(wf_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int32_t fail(wf_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return st;
+}
+
+int32_t ok() {
+  g_detail.clear();
+  return WF_OK;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(WF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define WF_CHECK_PTR(p)                                                      \
+  do {                                                                       \
+    if (!(p)) return fail(WF_ERR_INVALID_ARG, "%s is NULL", #p);             \
+    if (!aligned16(p)) return fail(WF_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+#define WF_CHECK_OPT_PTR(p)                                                  \
+  do {                                                                       \
+    if ((p) && !aligned16(p)) return fail(WF_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+// Largest element count of one [B][Hh][N][D] tensor the kernels index with
+// 64-bit offsets but 32-bit per-head offsets: N * D must fit in int32.
+bool sizes_ok(long long B, long long Hh, long long N, long long D) {
+  if (B < 1 || Hh < 1 || N < 1 || D < 1) return false;
+  if (N * D >= (1ll << 31)) return false;
+  if (B * Hh >= (1ll << 24)) return false;
+  return true;
+}
+
+// -------------------------------------------------------------- timing state
+struct Rec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_pool_used = 0;
+long long g_dropped = 0;
+constexpr size_t kMaxRecs = 65536;
+
+hipEvent_t pool_event() {
+  if (g_pool_used < g_pool.size()) return g_pool[g_pool_used++];
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  g_pool.push_back(e);
+  ++g_pool_used;
+  return e;
+}
+
+}  // namespace
+
+namespace wf {
+
+int prof_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on) return -1;
+  if (g_recs.size() >= kMaxRecs) {
+    ++g_dropped;
+    return -1;
+  }
+  hipEvent_t a = pool_event(), b = pool_event();
+  if (!a || !b) return -1;
+  (void)hipEventRecord(a, s);
+  g_recs.push_back({name, a, b});
+  return (int)g_recs.size() - 1;
+}
+
+void prof_end(int slot, hipStream_t s) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (slot < (int)g_recs.size()) (void)hipEventRecord(g_recs[slot].b, s);
+}
+
+}  // namespace wf
+
+extern "C" {
+
+const char* wf_status_string(int32_t status) {
+  switch (status) {
+    case WF_OK: return "WF_OK";
+    case WF_ERR_INVALID_ARG: return "WF_ERR_INVALID_ARG";
+    case WF_ERR_UNSUPPORTED: return "WF_ERR_UNSUPPORTED";
+    case WF_ERR_WORKSPACE: return "WF_ERR_WORKSPACE";
+    case WF_ERR_BAD_INDEX: return "WF_ERR_BAD_INDEX";
+    case WF_ERR_HIP: return "WF_ERR_HIP";
+    default: return "WF_UNKNOWN_STATUS";
+  }
+}
+
+const char* wf_last_error_detail(void) { return g_detail.c_str(); }
+
+int32_t wf_abi_version(void) { return 1; }
+
+size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D) {
+  if (!sizes_ok(B, Hh, N, D)) return 0;
+  return wf::dense_workspace_bytes(B * Hh, N, D);
+}
+
+int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
+                      int32_t Hh, int32_t N, int32_t D, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  WF_CHECK_PTR(q);
+  WF_CHECK_PTR(k);
+  WF_CHECK_PTR(v);
+  WF_CHECK_PTR(o);
+  WF_CHECK_OPT_PTR(lse);
+  if (!sizes_ok(B, Hh, N, D))
+    return fail(WF_ERR_INVALID_ARG, "bad sizes B=%d Hh=%d N=%d D=%d", B, Hh, N, D);
+  if (D != 64 && D != 128) return fail(WF_ERR_UNSUPPORTED, "head dimension %d (64 or 128)", D);
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
+  const size_t need = wf::dense_workspace_bytes(B * Hh, N, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  WF_CHECK_PTR(workspace);
+  hipError_t e = wf::launch_dense(q, k, v, o, lse, B * Hh, N, D, scale, workspace,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dense launch");
+  return ok();
+}
+
+int32_t wf_vsa_num_cubes(int32_t T, int32_t H, int32_t W) {
+  if (T < 1 || H < 1 || W < 1) return 0;
+  const long long C = (long long)((T + 3) / 4) * ((H + 3) / 4) * ((W + 3) / 4);
+  return C > (1 << 20) ? 0 : (int32_t)C;
+}
+
+static int32_t vsa_check_sizes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D) {
+  if (T < 1 || H < 1 || W < 1)
+    return fail(WF_ERR_INVALID_ARG, "bad grid T=%d H=%d W=%d", T, H, W);
+  const int32_t C = wf_vsa_num_cubes(T, H, W);
+  if (C == 0) return fail(WF_ERR_INVALID_ARG, "grid %dx%dx%d too large", T, H, W);
+  const long long Np = (long long)C * 64;
+  if (!sizes_ok(B, Hh, Np, D))
+    return fail(WF_ERR_INVALID_ARG, "bad sizes B=%d Hh=%d padded tokens=%lld D=%d", B, Hh, Np, D);
+  if (D != 128) return fail(WF_ERR_UNSUPPORTED, "VSA head dimension %d (only 128)", D);
+  if (C > 4096) return fail(WF_ERR_UNSUPPORTED, "%d cubes (at most 4096)", C);
+  if ((long long)C * C >= (1ll << 31))
+    return fail(WF_ERR_UNSUPPORTED, "%d cubes: score matrix too large", C);
+  return WF_OK;
+}
+
+size_t wf_vsa_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D) {
+  if (vsa_check_sizes(B, Hh, T, H, W, D) != WF_OK) return 0;
+  return wf::vsa_layout(B * Hh, T, H, W, D).total;
+}
+
+int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v, int32_t B, int32_t Hh,
+                           int32_t T, int32_t H, int32_t W, int32_t D, float scale, int32_t topk,
+                           int32_t* idx, float* coarse_scores, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  WF_CHECK_PTR(q);
+  WF_CHECK_PTR(k);
+  WF_CHECK_PTR(v);
+  WF_CHECK_PTR(idx);
+  WF_CHECK_OPT_PTR(coarse_scores);
+  if (int32_t st = vsa_check_sizes(B, Hh, T, H, W, D)) return st;
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
+  const int32_t C = wf_vsa_num_cubes(T, H, W);
+  if (topk < 1 || topk > C) return fail(WF_ERR_INVALID_ARG, "topk %d outside [1, %d]", topk, C);
+  const size_t need = wf::vsa_layout(B * Hh, T, H, W, D).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  WF_CHECK_PTR(workspace);
+  hipError_t e = wf::launch_vsa_coarse(q, k, v, B * Hh, T, H, W, D, scale, topk, idx, coarse_scores,
+                                       workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "VSA coarse launch");
+  return ok();
+}
+
+int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t* idx, int32_t B,
+                    int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D, float scale,
+                    int32_t topk, float* o, float* lse, void* stream) {
+  WF_CHECK_PTR(idx);
+  WF_CHECK_PTR(o);
+  WF_CHECK_OPT_PTR(lse);
+  if (int32_t st = vsa_check_sizes(B, Hh, T, H, W, D)) return st;
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
+  const int32_t C = wf_vsa_num_cubes(T, H, W);
+  if (topk < 1 || topk > C) return fail(WF_ERR_INVALID_ARG, "topk %d outside [1, %d]", topk, C);
+  const wf::VsaLayout L = wf::vsa_layout(B * Hh, T, H, W, D);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                L.total);
+  WF_CHECK_PTR(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* val = getenv("WF_VALIDATE");
+  if (val && val[0] == '1') {
+    int bad = 0;
+    hipError_t e = wf::launch_vsa_check(idx, B * Hh, C, topk, const_cast<void*>(workspace), L.flag,
+                                        s, &bad);
+    if (e != hipSuccess) return hip_fail(e, "VSA plan check");
+    if (bad) return fail(WF_ERR_BAD_INDEX, "top-k plan has an index outside [0, %d) or a row that is not strictly ascending", C);
+  }
+  hipError_t e = wf::launch_vsa_fine(workspace, idx, B * Hh, T, H, W, D, scale, topk, o, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "VSA fine launch");
+  return ok();
+}
+
+int32_t wf_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (on) {
+    g_recs.clear();
+    g_pool_used = 0;
+    g_dropped = 0;
+  }
+  g_on = on != 0;
+  return ok();
+}
+
+int32_t wf_profile_query(const char* name, int64_t* launches, double* total_ms) {
+  if (!name || !launches || !total_ms) return fail(WF_ERR_INVALID_ARG, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_mu);
+  int64_t n = 0;
+  double tot = 0.0;
+  for (const Rec& r : g_recs) {
+    if (strcmp(r.name, name) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    tot += ms;
+    ++n;
+  }
+  if (n == 0) return fail(WF_ERR_INVALID_ARG, "no recorded launch of %s", name);
+  *launches = n;
+  *total_ms = tot;
+  return ok();
+}
+
+}  // extern "C"

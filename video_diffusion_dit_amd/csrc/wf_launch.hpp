@@ -1,0 +1,42 @@
+// Internal host-side interface between the C ABI (capi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace wf {
+
+// Per-kernel timing hooks (capi.cpp): when timing is enabled, a HIP event is
+// recorded on the launch stream before and after the launch.
+int prof_begin(const char* name, hipStream_t s);
+void prof_end(int slot, hipStream_t s);
+
+template <class F>
+hipError_t wf_launch(const char* name, hipStream_t s, F&& launch) {
+  const int slot = prof_begin(name, s);
+  launch();
+  const hipError_t e = hipGetLastError();
+  prof_end(slot, s);
+  return e;
+}
+
+// Dense attention.
+size_t dense_workspace_bytes(int BH, int N, int D);
+hipError_t launch_dense(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
+                        int N, int D, float scale, void* ws, hipStream_t s);
+
+// VSA workspace layout (byte offsets, each 256-byte aligned).
+struct VsaLayout {
+  int C;
+  size_t qc, kc, vct, qbar, kbar, scores, flag, total;
+};
+VsaLayout vsa_layout(int BH, int T, int H, int W, int D);
+hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH, int T, int H,
+                             int W, int D, float scale, int topk, int* idx, float* scores_out,
+                             void* ws, hipStream_t s);
+hipError_t launch_vsa_check(const int* idx, int BH, int C, int topk, void* ws, size_t flag_off,
+                            hipStream_t s, int* bad);
+hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H, int W, int D,
+                           float scale, int topk, float* o, float* lse, hipStream_t s);
+
+}  // namespace wf
