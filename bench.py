@@ -33,8 +33,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (used for profiler runs)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="before timing, run one plain device copy of this many MiB (a known-size "
+                        "kernel that calibrates the profiler's HBM byte counters)")
     return p.parse_args()
 
 
@@ -66,7 +69,7 @@ def vsa_bytes(wl, C) -> dict:
 
 
 def cpu_baseline(seconds: float) -> dict:
-    """The fp64 oracle on a bounded sample of the dense workload: query rows of one head."""
+    """The fp64 oracle on a bounded sample of the dense workload: whole heads, about `seconds` of CPU."""
     import numpy as np
     import oracle
     import synth
@@ -76,22 +79,22 @@ def cpu_baseline(seconds: float) -> dict:
     except Exception:
         threads = os.cpu_count() or 1
     wl = synth.WORKLOADS[DENSE]
-    q = synth.bits_to_f64(synth.make_slice(wl, "q", 0, 0))
-    k = synth.bits_to_f64(synth.make_slice(wl, "k", 0, 0))
-    v = synth.bits_to_f64(synth.make_slice(wl, "v", 0, 0))
-    rows = 256
-    t0 = time.perf_counter()
-    oracle.attention(q, k, v, wl.scale, rows=np.arange(rows))
-    probe = time.perf_counter() - t0
-    rows = int(min(wl.N, max(256, rows * (seconds / max(probe, 1e-3)))))
-    t0 = time.perf_counter()
-    oracle.attention(q, k, v, wl.scale, rows=np.arange(rows))
-    dt = time.perf_counter() - t0
-    flops = 4.0 * rows * wl.N * wl.D
+    phi = synth.field_for(wl)
+    heads, dt = 0, 0.0
+    for bh in range(wl.B * wl.Hh):          # whole heads until the time budget is spent
+        b, h = divmod(bh, wl.Hh)
+        q, k, v = (synth.bits_to_f64(synth.make_slice(wl, t, b, h, phi)) for t in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, wl.scale)
+        dt += time.perf_counter() - t0
+        heads += 1
+        if dt >= seconds:
+            break
+    flops = 4.0 * heads * wl.N * wl.N * wl.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle, dense attention of {rows} query rows x {wl.N} keys x d{wl.D} "
-                      f"of head (0,0) of the {DENSE} workload ({dt:.1f} s); "
-                      f"ms per full dense call extrapolated: {dt * 1e3 * wl.B * wl.Hh * wl.N / rows:.0f}",
+            "sample": f"fp64 numpy oracle, dense attention of {heads} whole head(s) "
+                      f"({wl.N} x {wl.N} x d{wl.D}) of the {DENSE} workload, {dt:.1f} s; "
+                      f"one full dense call extrapolated: {dt / heads * wl.B * wl.Hh:.0f} s",
             "host_cpus": os.cpu_count()}
 
 
@@ -131,6 +134,13 @@ def main():
         wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
         wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
 
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

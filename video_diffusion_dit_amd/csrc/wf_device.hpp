@@ -7,10 +7,18 @@
 namespace wf {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+// The running maximum used as the softmax reference is only raised when a new
+// score exceeds it by more than this many powers of two; until then the
+// probabilities stay below 2^kLazy (safe in bf16 and fp32) and the O / l
+// accumulators need no rescaling.  O and l share the reference, so the final
+// O / l is unchanged (an exact identity, not an approximation).
+constexpr float kLazy = 8.f;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -112,6 +120,10 @@ struct Tile {
   }
 };
 
+struct P4 {
+  bf16x2 v[4];
+};
+
 // Per-wavefront attention state for 32 query rows.
 template <int D>
 struct RowState {
@@ -160,34 +172,47 @@ struct RowState {
     using T = Tile<D, 1>;
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = wave_max_pair(mx);
-    const float mnew = fmaxf(m, mx * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
-    bf16x8 p[4];
-    float ls = 0.f;
+    for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);  // v_max3 chain
+    mx = wave_max_pair(mx) * sl2;
+    if (__ballot(mx > m + kLazy)) {  // wave-uniform: raise the reference, rescale O and l
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      l *= alpha;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const __bf16 b0 = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, -mnew));
-      const __bf16 b1 = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, -mnew));
-      p[r / 8][r % 8] = b0;
-      p[2 + r / 8][r % 8] = b1;
-      ls += (float)b0 + (float)b1;
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
     }
-    l = l * alpha + ls;
+    const float nm = -m;
+    bf16x2 p2[16];  // probabilities, two per register, in score-register order
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int r = 0; r < 8; ++r) {
+      p2[r] = __builtin_convertvector(
+          (f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * r], sl2, nm)),
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * r + 1], sl2, nm))}, bf16x2);
+      p2[8 + r] = __builtin_convertvector(
+          (f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * r], sl2, nm)),
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * r + 1], sl2, nm))}, bf16x2);
+    }
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    float la = 0.f, lb = 0.f;  // row sum of the bf16 probabilities (what the MFMA consumes)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+    for (int i = 0; i < 16; i += 2) {
+      la = __builtin_amdgcn_fdot2_f32_bf16(p2[i], one2, la, false);
+      lb = __builtin_amdgcn_fdot2_f32_bf16(p2[i + 1], one2, lb, false);
+    }
+    l += la + lb;
     const uint16_t* vt = lds + T::KELEMS;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
+    for (int ks = 0; ks < 4; ++ks) {
+      const int base = (ks / 2) * 8 + (ks % 2) * 4;
+      const bf16x8 p = __builtin_bit_cast(bf16x8, P4{p2[base], p2[base + 1], p2[base + 2], p2[base + 3]});
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(vt + (b * 32 + j) * T::VSTR + ks * 16 + half * 8));
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks], o[b], 0, 0, 0);
-      }
+      for (int b = 0; b < DB; ++b)
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(*reinterpret_cast<const uint4*>(vt + (b * 32 + j) * T::VSTR + ks * 16 + half * 8)),
+            p, o[b], 0, 0, 0);
     }
   }
 
