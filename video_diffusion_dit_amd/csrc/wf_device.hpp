@@ -120,6 +120,10 @@ struct Tile {
   }
 };
 
+__device__ __forceinline__ void wait_tile_copies() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's global->LDS copies landed
+}
+
 struct P4 {
   bf16x2 v[4];
 };
