@@ -11,11 +11,15 @@ records on the launch stream around each kernel.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import subprocess
 import sys
 import time
+from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -24,6 +28,30 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 DENSE = "dense_480p_cfg"
 VSA = "vsa_480p"
+# HBM traffic of the dense kernel, measured with rocprofv3 FETCH_SIZE / WRITE_SIZE; used only while
+# the kernel sources hash to the value recorded with the measurement
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_fwd_480p_cfg.json")
+DENSE_SOURCES = [os.path.join(ROOT, "video_diffusion_dit_amd", "csrc", f) for f in ("dense.hip", "wf_device.hpp")]
+
+
+def sources_sha256(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per launch of wf_dense_fwd from the committed counter summary, or None if stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sources_sha256(DENSE_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
 
 
 def parse():
@@ -35,6 +63,8 @@ def parse():
                    help="skip timing the CPU oracle (used for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--summarize", metavar="ROCPROF_DIR", default=None,
+                   help="print a text summary of rocprofv3 CSV output under ROCPROF_DIR and exit")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB (a known-size "
                         "kernel that calibrates the profiler's HBM byte counters)")
@@ -98,8 +128,34 @@ def cpu_baseline(seconds: float) -> dict:
             "host_cpus": os.cpu_count()}
 
 
+def _short(name: str) -> str:
+    base = name.split("(")[0]
+    return base.replace("void ", "").strip()
+
+
+def summarize(rocprof_dir: str) -> None:
+    """Summarise rocprofv3 --kernel-trace --stats and --pmc CSV files (no GPU needed)."""
+    for path in sorted(glob.glob(os.path.join(rocprof_dir, "**", "*_kernel_stats.csv"), recursive=True)):
+        print(f"# kernel stats: {os.path.relpath(path, rocprof_dir)}")
+        print(f"{'kernel':44s} {'calls':>6s} {'avg_ms':>10s} {'min_ms':>10s} {'max_ms':>10s} {'pct':>6s}")
+        for r in csv.DictReader(open(path)):
+            print(f"{_short(r['Name'])[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:10.4f} "
+                  f"{float(r['MinNs']) / 1e6:10.4f} {float(r['MaxNs']) / 1e6:10.4f} {float(r['Percentage']):6.2f}")
+    for path in sorted(glob.glob(os.path.join(rocprof_dir, "**", "*_counter_collection.csv"), recursive=True)):
+        print(f"# counters: {os.path.relpath(path, rocprof_dir)} (mean per dispatch)")
+        agg = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            agg[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for k, cs in agg.items():
+            vals = "  ".join(f"{c}={sum(v) / len(v):.6g}" for c, v in sorted(cs.items()))
+            print(f"{k[:44]:44s} n={len(next(iter(cs.values())))}  {vals}")
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -198,7 +254,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": dense_tf / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "dense": {
             "ms_per_call": ms_dense,
