@@ -201,71 +201,79 @@ __global__ void __launch_bounds__(256) wf_vsa_topk(const float* __restrict__ s,
 }
 
 // ---------------------------------------------------------------- fine stage
-// One workgroup (2 wavefronts) per (bh, query cube): 64 query slots against the
-// 64 slots of each selected key cube, one cube per LDS stage.
+// One workgroup (2 wavefronts x 32 query slots) per (bh, query cube); it walks
+// the k selected key cubes, one cube (64 keys) per tile.  K and V^T of the
+// current cube sit in one K slot and one V slot of LDS (32 KiB, so several
+// workgroups share a CU and hide each other's latency).  The slots have
+// separate lifetimes: the copy of the next K cube starts as soon as both
+// wavefronts have their scores, the copy of the next V cube as soon as both
+// have accumulated P V; each copy lands behind the other half of the tile's
+// work.  Padded key slots of edge cubes are masked; output rows are scattered
+// back to grid order, padded query slots are not written.
 template <int D>
-__global__ void __launch_bounds__(128) wf_vsa_fine_fwd(
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vct, const int* __restrict__ idx, float* __restrict__ o,
     float* __restrict__ lse, Grid3 g, int k, float sl2) {
-  using T = Tile<D, 2>;
-  __shared__ __align__(16) uint16_t lds[2 * T::STAGE];
+  constexpr int DB = D / 32, NPV = Pairs<D>::NPV, NQK = Pairs<D>::NQK;
+  __shared__ __align__(16) char ks[Swz<D>::KB];
+  __shared__ __align__(16) char vs[Swz<D>::VB];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, j = lane % 32, half = lane / 32;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / g.C, c = item % g.C;
   const long cube_base = (long)bh * g.C;
   const int* plan = idx + ((long)bh * g.C + c) * k;
-
   const int slot = wave * 32 + j;
-  RowState<D> st;
-  st.init(qc + ((cube_base + c) * 64 + slot) * D, half);
 
-  T tile;
-  auto src = [&](int t, const uint16_t*& kg, const uint16_t*& vg) {
-    const long cc = cube_base + plan[t];
-    kg = kc + cc * 64 * D;
-    vg = vct + cc * D * 64;
-  };
-  const uint16_t *kg, *vg;
-  src(0, kg, vg);
-  tile.fetch(kg, 64, vg, 64, tid);
-  tile.stash(lds, tid);
-  __syncthreads();
+  bf16x8 qop[D / 16];
+  {
+    const uint16_t* qr = qc + ((cube_base + c) * 64 + slot) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kk * 16 + half * 8));
+  }
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  f32x16 s0, s1;
+  bf16x2 p2[16];
+
+  int cur = plan[0];
+  tile_copy<D, 2>(kc + (cube_base + cur) * 64 * D, 64, ks, vct + (cube_base + cur) * D * 64, 64, vs, wave, lane);
   for (int t = 0; t < k; ++t) {
-    if (t + 1 < k) {
-      src(t + 1, kg, vg);
-      tile.fetch(kg, 64, vg, 64, tid);
-    }
-    const uint16_t* cur = lds + (t & 1) * T::STAGE;
-    f32x16 s0, s1;
-    st.scores(cur, j, half, s0, s1);
+    wait_tile_copies();  // V(t) (and, at t = 0, K(t)) landed
+    __syncthreads();
+    mfma_run<D, NPV, NPV + NQK>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
+    __syncthreads();                                                       // K slot free
+    const int nxt = t + 1 < k ? plan[t + 1] : -1;
+    if (nxt >= 0) tile_copy<D, 2>(kc + (cube_base + nxt) * 64 * D, 64, ks, nullptr, 0, nullptr, wave, lane);
     int kt, kh, kw;
-    cube_coords(g, plan[t], kt, kh, kw);
+    cube_coords(g, cur, kt, kh, kw);
     const int lt = g.T - 4 * kt, lh = g.H - 4 * kh, lw = g.W - 4 * kw;
     if (lt < 4 || lh < 4 || lw < 4) {  // edge cube: mask padded key slots
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int sl = key_row(kb, r, half);
-          const bool ok = (sl >> 4) < lt && ((sl >> 2) & 3) < lh && (sl & 3) < lw;
-          if (!ok) (kb == 0 ? s0 : s1)[r] = -INFINITY;
-        }
+        const int a = key_row(0, r, half), b = key_row(1, r, half);
+        if (!((a >> 4) < lt && ((a >> 2) & 3) < lh && (a & 3) < lw)) s0[r] = -INFINITY;
+        if (!((b >> 4) < lt && ((b >> 2) & 3) < lh && (b & 3) < lw)) s1[r] = -INFINITY;
       }
     }
-    st.update(cur, j, half, s0, s1, sl2);
-    if (t + 1 < k) tile.stash(lds + ((t + 1) & 1) * T::STAGE, tid);
-    __syncthreads();
+    softmax_tile<DB>(s0, s1, sl2, m, l, oacc, p2);
+    mfma_run<D, 0, NPV>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // O += P V(t)
+    wait_tile_copies();                                            // K(t+1) landed
+    __syncthreads();                                               // V slot free, K(t+1) visible
+    if (nxt >= 0)
+      tile_copy<D, 2>(nullptr, 0, nullptr, vct + (cube_base + nxt) * D * 64, 64, vs, wave, lane);
+    cur = nxt;
   }
-  const float l = st.finish();
   int ct, ch, cw;
   cube_coords(g, c, ct, ch, cw);
   const int tok = slot_token(g, ct, ch, cw, slot);
-  if (tok >= 0) {
-    const long row = (long)bh * g.T * g.H * g.W + tok;
-    st.store(o + row * D, half);
-    if (lse && half == 0) lse[row] = l;
-  }
+  const long row = (long)bh * g.T * g.H * g.W + tok;
+  const float lse_row = finish_store<DB>(oacc, m, l, tok >= 0 ? o + row * D : nullptr, half);
+  if (lse && tok >= 0 && half == 0) lse[row] = lse_row;
 }
 
 // ---------------------------------------------------------------- plan check

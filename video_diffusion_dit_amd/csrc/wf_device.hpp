@@ -1,4 +1,15 @@
 // Device-side building blocks shared by the dense and VSA kernels (gfx950 only).
+//
+// The attention tile math, per wavefront owning 32 query rows and one tile of
+// 64 keys, with lane L (j = L % 32, half = L / 32):
+//   S^T (64 x 32) = K_tile (64 x D) . Q^T (D x 32)      two 32x32 blocks, MFMA 32x32x16 bf16
+//     A operand: K rows from LDS; B operand: Q in registers.  Lane L ends up
+//     holding query j and key rows 8*(r/4) + 4*half + r%4 of each block, so a
+//     query's row max / row sum only combines lanes L and L^32.
+//   online softmax in the exp2 domain with a lazily raised reference max;
+//   O^T (D x 32) += V^T_tile (D x 64) . P^T (64 x 32)    D/32 blocks x 4 k-steps
+//     A operand: V^T rows from LDS (keys in perm16 order); B operand: the
+//     probabilities straight from the score registers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,74 +62,10 @@ __device__ __forceinline__ float wave_max_pair(float x) {  // max over lanes L a
   return fmaxf(x, __shfl_xor(x, 32));
 }
 
-// One wavefront owns 32 query rows; a workgroup of NW wavefronts shares K and
-// V^T tiles of BN = 64 keys staged through LDS (double buffered, register
-// prefetch of the next tile while the current one is consumed).
-//
-// Per wavefront and tile, with lane L (j = L % 32, half = L / 32):
-//   S^T (64 x 32) = K_tile (64 x D) . Q^T (D x 32)   two 32x32 blocks, MFMA 32x32x16 bf16
-//     - A operand: K rows from LDS, B operand: Q held in registers;
-//     - lane L ends up holding query j and key rows 8*(r/4) + 4*half + r%4 of
-//       each block, so the row max / sum of query j needs only lanes L, L^32.
-//   online softmax in the exp2 domain: m (running max, log2 units), l (sum of
-//     the bf16-rounded probabilities, per lane, merged at the end);
-//   O^T (D x 32) += V^T_tile (D x 64) . P^T (64 x 32)  D/32 blocks x 4 k-steps
-//     - A operand: V^T rows from LDS (keys stored in perm16 order),
-//       B operand: P^T straight from the score registers.
-template <int D, int NW>
-struct Tile {
-  static constexpr int BN = 64;
-  static constexpr int NT = NW * 64;
-  static constexpr int KSTR = D + 8;          // LDS row stride (elements) of the K tile
-  static constexpr int VSTR = BN + 8;         // LDS row stride of the V^T tile
-  static constexpr int KELEMS = BN * KSTR;
-  static constexpr int VELEMS = D * VSTR;
-  static constexpr int STAGE = KELEMS + VELEMS;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int KCH = BN * D / 8 / NT;  // 16-byte chunks per thread, K tile
-  static constexpr int VCH = D * BN / 8 / NT;  // same, V^T tile
-  static constexpr int KROWCH = D / 8;         // chunks per K row
-  static constexpr int VROWCH = BN / 8;        // chunks per V^T row
-  static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
-
-  uint4 kreg[KCH];
-  uint4 vreg[VCH];
-
-  // Global -> registers.  kg: row-major [BN][D] (rows >= krows read as zero);
-  // vg: V^T rows of BN keys, row d at vg + d * vld.
-  __device__ __forceinline__ void fetch(const uint16_t* __restrict__ kg, int krows,
-                                        const uint16_t* __restrict__ vg, long vld, int tid) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = i * NT + tid;
-      const int r = id / KROWCH, c = id % KROWCH;
-      kreg[i] = (r < krows) ? *reinterpret_cast<const uint4*>(kg + (long)r * D + c * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int id = i * NT + tid;
-      const int d = id / VROWCH, c = id % VROWCH;
-      vreg[i] = *reinterpret_cast<const uint4*>(vg + (long)d * vld + c * 8);
-    }
-  }
-
-  // Registers -> LDS stage.
-  __device__ __forceinline__ void stash(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = i * NT + tid;
-      const int r = id / KROWCH, c = id % KROWCH;
-      *reinterpret_cast<uint4*>(lds + r * KSTR + c * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int id = i * NT + tid;
-      const int d = id / VROWCH, c = id % VROWCH;
-      *reinterpret_cast<uint4*>(lds + KELEMS + d * VSTR + c * 8) = vreg[i];
-    }
-  }
-};
+// Key row (0..63 inside a tile) held by register r of score block kb in lane half `half`.
+__device__ __forceinline__ int key_row(int kb, int r, int half) {
+  return kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+}
 
 __device__ __forceinline__ void wait_tile_copies() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's global->LDS copies landed
@@ -128,123 +75,175 @@ struct P4 {
   bf16x2 v[4];
 };
 
-// Per-wavefront attention state for 32 query rows.
+// ------------------------------------------------------------------ LDS tiles
+// A K tile is [64 keys][D] bf16 and a V^T tile [D][64 keys] bf16, both
+// unpadded.  Each 16-byte chunk is XOR-swizzled within its row so that the 16
+// lanes of one ds_read_b128 quarter-wave (one chunk of 16 consecutive rows)
+// hit 16 distinct 16-byte bank groups of gfx950's 64-bank LDS.
 template <int D>
-struct RowState {
-  static constexpr int KK = D / 16;  // k-steps of the QK^T product
-  static constexpr int DB = D / 32;  // 32-row blocks of O^T
-  bf16x8 qop[KK];
-  f32x16 o[DB];
-  float m;  // running max of scale*log2(e)*s (log2 units)
-  float l;  // this lane's share of the running sum
-
-  // q_row: this lane's query row (D bf16) or nullptr for a zero row.
-  __device__ __forceinline__ void init(const uint16_t* __restrict__ q_row, int half) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      uint4 u = q_row ? *reinterpret_cast<const uint4*>(q_row + kk * 16 + half * 8)
-                      : make_uint4(0, 0, 0, 0);
-      qop[kk] = as_bf16x8(u);
-    }
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
-    m = -INFINITY;
-    l = 0.f;
+struct Swz {
+  static constexpr int KB = 64 * D * 2;  // K tile bytes
+  static constexpr int VB = D * 64 * 2;  // V^T tile bytes
+  static constexpr int KCPR = D / 8;     // 16-byte chunks per K row
+  __host__ __device__ static constexpr int kslot(int r, int c) {
+    return KCPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
   }
+  __host__ __device__ static constexpr int vslot(int d, int c) { return c ^ ((d >> 1) & 7); }
+};
 
-  // S^T for the 64 keys of the LDS stage.
-  __device__ __forceinline__ void scores(const uint16_t* lds, int j, int half, f32x16& s0,
-                                         f32x16& s1) const {
-    using T = Tile<D, 1>;
+// NWC wavefronts (w = 0..NWC-1) copy one K tile and/or one V^T tile global ->
+// LDS with global_load_lds_dwordx4 (each instruction lays 64 lanes x 16 bytes
+// contiguously at a wave-uniform LDS address).  K rows >= krows are not read:
+// row krows-1 is fetched in their place and those keys are masked later.
+// kg / vg may be null to skip that tile.  V^T row d starts at vg + d * vld.
+template <int D, int NWC>
+__device__ __forceinline__ void tile_copy(const uint16_t* __restrict__ kg, int krows, char* kdst,
+                                          const uint16_t* __restrict__ vg, long vld, char* vdst, int w,
+                                          int lane) {
+  constexpr int KPIECES = Swz<D>::KB / 1024, VPIECES = Swz<D>::VB / 1024, CPR = Swz<D>::KCPR;
+  static_assert(KPIECES % NWC == 0 && VPIECES % NWC == 0, "pieces per wavefront");
+  if (kg) {
+#pragma unroll
+    for (int i = 0; i < KPIECES / NWC; ++i) {
+      const int g = i * NWC + w, P = g * 64 + lane;
+      const int r = P / CPR, c = Swz<D>::kslot(r, P % CPR);  // the swizzle is an involution in c
+      const int rr = min(r, krows - 1);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kg + (long)rr * D + c * 8),
+                                       (__attribute__((address_space(3))) void*)(kdst + g * 1024), 16, 0, 0);
+    }
+  }
+  if (vg) {
+#pragma unroll
+    for (int i = 0; i < VPIECES / NWC; ++i) {
+      const int g = i * NWC + w, P = g * 64 + lane;
+      const int d = P / 8, c = Swz<D>::vslot(d, P % 8);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vg + (long)d * vld + c * 8),
+                                       (__attribute__((address_space(3))) void*)(vdst + g * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// --------------------------------------------------------- MFMA operand runs
+// The MFMAs of one tile as a numbered list of (LDS operand, MFMA) pairs:
+// [0, NPV) are P V (operand = V^T rows), [NPV, NPV + NQK) are K Q^T
+// (operand = K rows).
+template <int D>
+struct Pairs {
+  static constexpr int NPV = 4 * (D / 32);
+  static constexpr int NQK = 2 * (D / 16);
+};
+
+template <int D>
+__device__ __forceinline__ uint4 mfma_operand(int i, const char* vt, const char* kt, int j, int half) {
+  constexpr int NPV = Pairs<D>::NPV;
+  if (i < NPV) {  // ks = i / (D/32), block b = i % (D/32)
+    const int ks = i / (D / 32), b = i % (D / 32), d = b * 32 + j, c = ks * 2 + half;
+    return *reinterpret_cast<const uint4*>(vt + d * 128 + Swz<D>::vslot(d, c) * 16);
+  }
+  const int kk = (i - NPV) / 2, r = ((i - NPV) % 2) * 32 + j, c = kk * 2 + half;
+  return *reinterpret_cast<const uint4*>(kt + r * (D * 2) + Swz<D>::kslot(r, c) * 16);
+}
+
+template <int D>
+__device__ __forceinline__ void mfma_pair(int i, uint4 a, const bf16x2* p2, const bf16x8* qop, f32x16* o,
+                                          f32x16& s0, f32x16& s1) {
+  constexpr int NPV = Pairs<D>::NPV;
+  if (i < NPV) {
+    const int ks = i / (D / 32), b = i % (D / 32);
+    const int base = (ks / 2) * 8 + (ks % 2) * 4;
+    const bf16x8 p = __builtin_bit_cast(bf16x8, P4{p2[base], p2[base + 1], p2[base + 2], p2[base + 3]});
+    o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), p, o[b], 0, 0, 0);
+  } else {
+    const int kk = (i - NPV) / 2;
+    if ((i - NPV) % 2 == 0) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qop[kk], s0, 0, 0, 0);
+    else s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qop[kk], s1, 0, 0, 0);
+  }
+}
+
+// Pairs [I0, I1): operands are read PF pairs ahead of the MFMA that consumes
+// them; each step is fenced with sched_barrier so the compiler keeps that
+// distance (it otherwise reads each operand right before its MFMA and the LDS
+// latency stalls the matrix pipe).  Scores are zeroed first if the run
+// contains K Q^T pairs.
+template <int D, int I0, int I1>
+__device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
+                                         f32x16* o, f32x16& s0, f32x16& s1, int j, int half) {
+  constexpr int PF = 4, R = PF + 1, NP = I1 - I0;
+  if constexpr (I1 > Pairs<D>::NPV) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + j * T::KSTR + kk * 16 + half * 8));
-      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + (32 + j) * T::KSTR + kk * 16 + half * 8));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[kk], s1, 0, 0, 0);
-    }
   }
-
-  // Online softmax update with scores s0/s1 (masked entries already -inf),
-  // then O^T += V^T P^T from the LDS stage.
-  __device__ __forceinline__ void update(const uint16_t* lds, int j, int half, const f32x16& s0,
-                                         const f32x16& s1, float sl2) {
-    using T = Tile<D, 1>;
-    float mx = -INFINITY;
+  uint4 ring[R];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);  // v_max3 chain
-    mx = wave_max_pair(mx) * sl2;
-    if (__ballot(mx > m + kLazy)) {  // wave-uniform: raise the reference, rescale O and l
-      const float mnew = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      l *= alpha;
+  for (int u = 0; u < PF && u < NP; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, j, half);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
-    }
-    const float nm = -m;
-    bf16x2 p2[16];  // probabilities, two per register, in score-register order
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p2[r] = __builtin_convertvector(
-          (f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * r], sl2, nm)),
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * r + 1], sl2, nm))}, bf16x2);
-      p2[8 + r] = __builtin_convertvector(
-          (f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * r], sl2, nm)),
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * r + 1], sl2, nm))}, bf16x2);
-    }
-    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-    float la = 0.f, lb = 0.f;  // row sum of the bf16 probabilities (what the MFMA consumes)
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      la = __builtin_amdgcn_fdot2_f32_bf16(p2[i], one2, la, false);
-      lb = __builtin_amdgcn_fdot2_f32_bf16(p2[i + 1], one2, lb, false);
-    }
-    l += la + lb;
-    const uint16_t* vt = lds + T::KELEMS;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int base = (ks / 2) * 8 + (ks % 2) * 4;
-      const bf16x8 p = __builtin_bit_cast(bf16x8, P4{p2[base], p2[base + 1], p2[base + 2], p2[base + 3]});
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(vt + (b * 32 + j) * T::VSTR + ks * 16 + half * 8)),
-            p, o[b], 0, 0, 0);
-    }
+  for (int i = 0; i < NP; ++i) {
+    if (i + PF < NP) ring[(i + PF) % R] = mfma_operand<D>(I0 + i + PF, vt, kt, j, half);
+    mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
 
-  // Final normalisation.  Returns this query's lse (natural log); scales o by 1/l.
-  __device__ __forceinline__ float finish() {
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = 1.f / lt;
+// ------------------------------------------------------------- softmax tile
+// Online softmax step for one tile of scores s0 / s1 (masked entries already
+// -inf): raises the reference max m lazily (rescaling O and l when it does),
+// writes the bf16 probabilities p2 (two per register, score-register order)
+// and adds their sum to l (the bf16-rounded values the PV MFMA consumes).
+template <int DB>
+__device__ __forceinline__ void softmax_tile(const f32x16& s0, const f32x16& s1, float sl2, float& m, float& l,
+                                             f32x16* o, bf16x2* p2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);  // v_max3 chain
+  mx = wave_max_pair(mx) * sl2;
+  if (__ballot(mx > m + kLazy)) {  // wave-uniform: raise the reference, rescale O and l
+    const float mnew = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    l *= alpha;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[b][r] *= inv;
-    return (m + __builtin_amdgcn_logf(lt)) * kLn2;
+      for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
   }
+  const float nm = -m;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    p2[r] = __builtin_convertvector((f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * r], sl2, nm)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * r + 1], sl2, nm))},
+                                    bf16x2);
+    p2[8 + r] = __builtin_convertvector((f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * r], sl2, nm)),
+                                                __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * r + 1], sl2, nm))},
+                                        bf16x2);
+  }
+  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+  float la = 0.f, lb = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    la = __builtin_amdgcn_fdot2_f32_bf16(p2[i], one2, la, false);
+    lb = __builtin_amdgcn_fdot2_f32_bf16(p2[i + 1], one2, lb, false);
+  }
+  l += la + lb;
+}
 
-  // Store the 32 x D block: this lane writes its query row's 4*DB float4s.
-  __device__ __forceinline__ void store(float* __restrict__ o_row, int half) const {
+// Final normalisation and store of one wavefront's 32 x D output block: the
+// lane writes its query row's DB*4 float4s (orow null: nothing stored).
+// Returns lse (natural log).
+template <int DB>
+__device__ __forceinline__ float finish_store(const f32x16* o, float m, float l, float* __restrict__ orow,
+                                              int half) {
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.f / lt;
+  if (orow) {
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq)
-        *reinterpret_cast<float4*>(o_row + b * 32 + rq * 8 + half * 4) =
-            make_float4(o[b][rq * 4 + 0], o[b][rq * 4 + 1], o[b][rq * 4 + 2], o[b][rq * 4 + 3]);
+        *reinterpret_cast<float4*>(orow + b * 32 + rq * 8 + half * 4) =
+            make_float4(o[b][rq * 4] * inv, o[b][rq * 4 + 1] * inv, o[b][rq * 4 + 2] * inv, o[b][rq * 4 + 3] * inv);
   }
-};
-
-// Key row (0..63 inside the stage) held by register r of block kb in lane half `half`.
-__device__ __forceinline__ int key_row(int kb, int r, int half) {
-  return kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+  return (m + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
 }  // namespace wf
