@@ -24,12 +24,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-// The running maximum used as the softmax reference is only raised when a new
-// score exceeds it by more than this many powers of two; until then the
-// probabilities stay below 2^kLazy (safe in bf16 and fp32) and the O / l
-// accumulators need no rescaling.  O and l share the reference, so the final
-// O / l is unchanged (an exact identity, not an approximation).
-constexpr float kLazy = 8.f;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -186,27 +180,9 @@ __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const b
 }
 
 // ------------------------------------------------------------- softmax tile
-// Online softmax step for one tile of scores s0 / s1 (masked entries already
-// -inf): raises the reference max m lazily (rescaling O and l when it does),
-// writes the bf16 probabilities p2 (two per register, score-register order)
-// and adds their sum to l (the bf16-rounded values the PV MFMA consumes).
-template <int DB>
-__device__ __forceinline__ void softmax_tile(const f32x16& s0, const f32x16& s1, float sl2, float& m, float& l,
-                                             f32x16* o, bf16x2* p2) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);  // v_max3 chain
-  mx = wave_max_pair(mx) * sl2;
-  if (__ballot(mx > m + kLazy)) {  // wave-uniform: raise the reference, rescale O and l
-    const float mnew = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
-  }
+// Probabilities of one tile against the reference m: p = 2^(s*sl2 - m) in bf16
+// (two per register, score-register order); returns this lane's sum of them.
+__device__ __forceinline__ float tile_probs(const f32x16& s0, const f32x16& s1, float sl2, float m, bf16x2* p2) {
   const float nm = -m;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
@@ -224,7 +200,39 @@ __device__ __forceinline__ void softmax_tile(const f32x16& s0, const f32x16& s1,
     la = __builtin_amdgcn_fdot2_f32_bf16(p2[i], one2, la, false);
     lb = __builtin_amdgcn_fdot2_f32_bf16(p2[i + 1], one2, lb, false);
   }
-  l += la + lb;
+  return la + lb;
+}
+
+// Online softmax step for one tile of scores s0 / s1 (masked entries -inf).
+// bf16 shares fp32's exponent range, so probabilities may grow far above the
+// reference m before anything is at risk: a lane's tile sum is allowed up to
+// 2^64 (O and l accumulate in fp32, whose range ends near 2^128).  The common path therefore skips the row max: it exponentiates
+// against the current reference and checks the tile's probability sum.  Only
+// when that sum exceeds 2^64 (or is inf / NaN) -- or on the first tile, when m is
+// still -inf -- does it take the row max, raise m, rescale O and l, and
+// recompute the tile.  O / l is unchanged by the choice of reference, and the
+// references are integers, so the bf16 probabilities do not depend on when
+// the reference was raised (they differ by exact powers of two).
+template <int DB>
+__device__ __forceinline__ void softmax_tile(const f32x16& s0, const f32x16& s1, float sl2, float& m, float& l,
+                                             f32x16* o, bf16x2* p2) {
+  float lt = tile_probs(s0, s1, sl2, m, p2);
+  if (__ballot(!(lt <= 0x1p64f))) {  // first tile (m = -inf gives inf/NaN) or a big jump
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+    mx = wave_max_pair(mx) * sl2;
+    const float mnew = fmaxf(m, ceilf(mx));  // integer references: a later raise rescales by a power of two
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+    lt = tile_probs(s0, s1, sl2, m, p2);
+  }
+  l += lt;
 }
 
 // Final normalisation and store of one wavefront's 32 x D output block: the
