@@ -61,7 +61,8 @@ class Workload:
         return 1.0 / float(np.sqrt(self.D))
 
 
-# The five workloads the measurements are quoted on.
+# The five measured configurations, plus dense attention on the 720p tensors and VSA at the
+# review's 78-of-624 operating point.
 WORKLOADS = {
     "dense_512_iid": Workload("dense_512_iid", 1, 2, 8, 8, 8, 64, False, 1,
                               note="dense MHA, 8x8x8 grid, d64, iid N(0,1)"),
@@ -73,6 +74,12 @@ WORKLOADS = {
                          note="VSA, 480p grid padded to 24x32x52, 624 cubes, top-32"),
     "vsa_720p": Workload("vsa_720p", 2, 40, 21, 45, 80, 128, True, 5, topk=64,
                          note="VSA, 720p grid padded to 24x48x80, 1440 cubes, top-64"),
+    # dense attention on the same 720p tensors (same seed) for comparison with VSA
+    "dense_720p_cfg": Workload("dense_720p_cfg", 2, 40, 21, 45, 80, 128, True, 5,
+                               note="dense MHA, 720p grid 21x45x80, CFG pair x 40 heads"),
+    # the page's operating point: 78 of 624 cubes (87.5% sparsity)
+    "vsa_480p_k78": Workload("vsa_480p_k78", 1, 40, 21, 30, 52, 128, True, 4, topk=78,
+                             note="VSA, 480p grid, 624 cubes, top-78 (the review's 87.5% sparsity)"),
 }
 
 

@@ -90,6 +90,20 @@ def test_dense_closed_forms_on_gpu(wf):
     assert np.abs(lse - math.log(wl.N)).max() <= 1e-4
 
 
+def test_dense_large_values_stay_finite(wf):
+    """|V| near 1e30 and logits near 1e3 together: the accumulators must not overflow."""
+    wl = synth.small_workload("bigv", 1, 1, 4, 8, 16, 128, structured=True, seed=10)
+    log("dense large V N=512 D=128")
+    q, k, v = synth.make_qkv(wl)
+    qb = synth.bf16_bits(synth.bits_to_f32(q) * 64.0)
+    vb = synth.bf16_bits(synth.bits_to_f32(v) * 1e30)
+    o, lse = run_dense(wf, qb, k, vb)
+    ref_o, _ = oracle.attention(synth.bits_to_f64(qb[0, 0]), synth.bits_to_f64(k[0, 0]),
+                                synth.bits_to_f64(vb[0, 0]), wl.scale)
+    assert np.isfinite(o).all()
+    assert_close(o[0, 0] / 1e30, ref_o / 1e30, "O large V (scaled by 1e-30)")
+
+
 def test_dense_large_logits_stay_finite(wf):
     """Q scaled x64 drives logits to ~1e3: a softmax without the running max overflows."""
     wl = synth.small_workload("big", 1, 1, 4, 8, 16, 128, structured=True, seed=9)
@@ -106,8 +120,9 @@ def test_dense_large_logits_stay_finite(wf):
 
 
 @pytest.mark.parametrize("name,heads", [("dense_480p_12h", [(0, 0), (0, 5), (0, 11)]),
-                                        ("dense_480p_cfg", [(0, 0), (0, 39), (1, 7), (1, 22)])])
-def test_dense_480p_sampled(wf, name, heads):
+                                        ("dense_480p_cfg", [(0, 0), (0, 39), (1, 7), (1, 22)]),
+                                        ("dense_720p_cfg", [(0, 1), (1, 30)])])
+def test_dense_full_shape_sampled(wf, name, heads):
     wl = synth.WORKLOADS[name]
     log(f"dense {name} B={wl.B} Hh={wl.Hh} N={wl.N} D={wl.D} (full launch, sampled rows)")
     q, k, v = synth.make_qkv(wl)

@@ -141,6 +141,19 @@ def test_vsa_480p_full(wf):
     check_fine(wl, q, k, v, g, tok, [(0, 39)])
 
 
+def test_vsa_480p_k78(wf):
+    """The review's operating point: 78 of 624 cubes kept."""
+    wl = synth.WORKLOADS["vsa_480p_k78"]
+    log(f"vsa {wl.name} B={wl.B} Hh={wl.Hh} topk={wl.topk} (all heads idx)")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    heads = [(0, h) for h in range(wl.Hh)]
+    ref, tok = coarse_ref(wl, q, k, heads, wl.topk)
+    check_scores_and_idx(g, ref, heads)
+    cubes = sorted(np.random.default_rng(78).choice(tok.shape[0], 24, replace=False).tolist() + [0, 623])
+    check_fine(wl, q, k, v, g, tok, [(0, 5), (0, 33)], cubes)
+
+
 def test_vsa_720p_full(wf):
     wl = synth.WORKLOADS["vsa_720p"]
     log(f"vsa {wl.name} B={wl.B} Hh={wl.Hh} grid {wl.T}x{wl.H}x{wl.W} topk={wl.topk} (all heads idx)")

@@ -204,20 +204,21 @@ __device__ __forceinline__ float tile_probs(const f32x16& s0, const f32x16& s1, 
 }
 
 // Online softmax step for one tile of scores s0 / s1 (masked entries -inf).
-// bf16 shares fp32's exponent range, so probabilities may grow far above the
-// reference m before anything is at risk: a lane's tile sum is allowed up to
-// 2^64 (O and l accumulate in fp32, whose range ends near 2^128).  The common path therefore skips the row max: it exponentiates
-// against the current reference and checks the tile's probability sum.  Only
-// when that sum exceeds 2^64 (or is inf / NaN) -- or on the first tile, when m is
-// still -inf -- does it take the row max, raise m, rescale O and l, and
-// recompute the tile.  O / l is unchanged by the choice of reference, and the
+// bf16 shares fp32's exponent range, so probabilities may exceed 1 (the
+// reference m may lag behind the row maximum) without loss: a lane's tile sum
+// is allowed up to 2^16, which keeps O and l (fp32) far from overflow for any
+// |V| below 2^100.  The common path therefore skips the row max: it
+// exponentiates against the current reference and checks the lane's
+// probability sum.  Only when that sum exceeds 2^16 (or is inf / NaN) -- or
+// on the first tile, when m is still -inf -- does it take the row max, raise
+// m, rescale O and l, and recompute the tile.  O / l is unchanged by the choice of reference, and the
 // references are integers, so the bf16 probabilities do not depend on when
 // the reference was raised (they differ by exact powers of two).
 template <int DB>
 __device__ __forceinline__ void softmax_tile(const f32x16& s0, const f32x16& s1, float sl2, float& m, float& l,
                                              f32x16* o, bf16x2* p2) {
   float lt = tile_probs(s0, s1, sl2, m, p2);
-  if (__ballot(!(lt <= 0x1p64f))) {  // first tile (m = -inf gives inf/NaN) or a big jump
+  if (__ballot(!(lt <= 0x1p16f))) {  // first tile (m = -inf gives inf/NaN) or a big jump
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
