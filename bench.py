@@ -65,6 +65,9 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--summarize", metavar="ROCPROF_DIR", default=None,
                    help="print a text summary of rocprofv3 CSV output under ROCPROF_DIR and exit")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the top-78 VSA record after the timed steps (profiling runs: keeps "
+                        "per-kernel averages to the step's own launches)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB (a known-size "
                         "kernel that calibrates the profiler's HBM byte counters)")
@@ -219,24 +222,25 @@ def main():
     wf.profile_enable(False)
 
     # extra record (not part of the step): VSA at the review's 78-of-624 operating point
-    k78 = synth.WORKLOADS["vsa_480p_k78"].topk
-    idx78 = torch.empty((wv.B, wv.Hh, C, k78), dtype=torch.int32, device=dev)
+    k78, k78_ms = synth.WORKLOADS["vsa_480p_k78"].topk, None
+    if not args.no_extra:
+        idx78 = torch.empty((wv.B, wv.Hh, C, k78), dtype=torch.int32, device=dev)
 
-    def vsa78():
-        wf.wf_vsa_coarse_topk(qv, kv, vv, grid, k78, idx=idx78, workspace=ws_v)
-        wf.wf_vsa_fine(ws_v, idx78, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
+        def vsa78():
+            wf.wf_vsa_coarse_topk(qv, kv, vv, grid, k78, idx=idx78, workspace=ws_v)
+            wf.wf_vsa_fine(ws_v, idx78, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
 
-    vsa78()
-    torch.cuda.synchronize()
-    wf.profile_enable(True)
-    for _ in range(max(3, args.steps // 2)):
         vsa78()
-    torch.cuda.synchronize()
-    k78_ms = {}
-    for name in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine"):
-        n, tot = wf.profile_query(name)
-        k78_ms[name] = tot / n
-    wf.profile_enable(False)
+        torch.cuda.synchronize()
+        wf.profile_enable(True)
+        for _ in range(max(3, args.steps // 2)):
+            vsa78()
+        torch.cuda.synchronize()
+        k78_ms = {}
+        for name in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine"):
+            n, tot = wf.profile_query(name)
+            k78_ms[name] = tot / n
+        wf.profile_enable(False)
 
     fl_d = dense_flops(wd)
     fl_v = vsa_flops(wv, C)
@@ -296,7 +300,7 @@ def main():
             "dense_equivalent_tflops": fl_d * wv.B / wd.B / (ms_vsa * 1e-3) / 1e12,
             "ideal_speedup": C / wv.topk,
         },
-        "vsa_k78": {
+        "vsa_k78": None if k78_ms is None else {
             "topk": k78,
             "ms_per_call": sum(k78_ms.values()),
             "kernel_ms": k78_ms,
