@@ -5,6 +5,8 @@
 // the grid, O = softmax(scale Q K^T) V per (batch, head), computed tile by tile
 // without materialising the score matrix; the softmax keeps a running row
 // maximum (section "Fixed-max softmax is a numerical contract").
+#include <type_traits>
+
 #include "wf_device.hpp"
 #include "wf_launch.hpp"
 
@@ -46,11 +48,12 @@ __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict
 // per workgroup.  Every wavefront alternates an MFMA phase (P(t-1) V(t-1) then
 // S(t) = K(t) Q^T) and a VALU phase (softmax of S(t)).  Half B runs one
 // barrier behind half A, so on every SIMD one wavefront is in its MFMA phase
-// while the other is in its VALU phase.  K(t) and V(t-1) are resident during
-// global phases 2t and 2t+1; in its VALU phase t half A copies K(t+1) and V(t)
-// global -> LDS directly (no staging registers) into the slots that K(t-1)
-// and V(t-2) left, and waits for them before the phase's closing barrier.
-// Within an MFMA phase the LDS operand reads run four MFMAs ahead of use.
+// (at raised issue priority) while the other is in its VALU phase.  K and V^T
+// tiles rotate through three LDS slots each: in its VALU phase t half A copies
+// K(t+2) and V(t+1) global -> LDS with buffer loads (no staging registers)
+// into the slots K(t-1) and V(t-2) left, and waits only for the previous
+// phase's copies, so each copy has about two phases to land.  Within an MFMA
+// phase the LDS operand reads run four MFMAs ahead of use.
 template <int D>
 __global__ void __launch_bounds__(512, 1)
 wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -59,11 +62,14 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   constexpr int DB = D / 32;
   __shared__ __align__(16) char kt0[Swz<D>::KB];
   __shared__ __align__(16) char kt1[Swz<D>::KB];
+  __shared__ __align__(16) char kt2[Swz<D>::KB];
   __shared__ __align__(16) char vt0[Swz<D>::VB];
   __shared__ __align__(16) char vt1[Swz<D>::VB];
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, j = lane % 32, half = lane / 32;
+  __shared__ __align__(16) char vt2[Swz<D>::VB];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, j = lane % 32,
+            half = lane / 32;
   const bool isB = wave >= 4;
-  const int wq = wave & 3;
+  const int wq = __builtin_amdgcn_readfirstlane(wave & 3);
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / nqt, qt = item % nqt;
   const long base = (long)bh * N;
@@ -88,27 +94,41 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
   for (int i = 0; i < 16; ++i) p2[i] = (bf16x2){(__bf16)0.f, (__bf16)0.f};
   // the first MFMA phase runs P V on zero probabilities: give it a zero V slot too
-  for (int i = tid; i < Swz<D>::VB / 16; i += 512) reinterpret_cast<uint4*>(vt1)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < Swz<D>::VB / 16; i += 512) reinterpret_cast<uint4*>(vt2)[i] = make_uint4(0, 0, 0, 0);
 
+  constexpr int KP = Swz<D>::KB / 1024 / 4, VP = Swz<D>::VB / 1024 / 4;  // copies per wavefront of half A
   const int nt = (N + 63) / 64;
+  // Three K slots and three V slots: tile t's K sits in slot t % 3, its V in slot t % 3.
+  // Prologue: K(0), then K(1) and V(0); K(0) must land before the first MFMA phase.
+  const CopyOffsets<D, 4> coff(wq, lane, Np);
+  const uint32_t vbytes = (uint32_t)D * Np * 2;  // one head's V^T
   if (!isB) {
-    tile_copy<D, 4>(kg, N, kt0, nullptr, 0, nullptr, wq, lane);
-    wait_tile_copies();
+    tile_copy<D, 4>(coff, kg, N, kt0, nullptr, 0, 0, nullptr, wq);
+    tile_copy<D, 4>(coff, nt > 1 ? kg + 64 * D : nullptr, N - 64, kt1, vg, Np, vbytes, vt0, wq);
   }
-  __syncthreads();
+  __syncthreads();  // its fence waits for all three copies
   if (isB) __syncthreads();  // half B runs one phase behind
 
-  // one MFMA phase and one VALU phase for tile t; kcur = K(t), vprev = V(t-1),
-  // knext / vfill receive K(t+1) / V(t)
-  auto phase_pair = [&](int t, const char* kcur, const char* vprev, char* knext, char* vfill) {
+  // one MFMA phase and one VALU phase for tile t; kcur = K(t), vprev = V(t-1).  In its VALU
+  // phase half A copies K(t+2) into knext and V(t+1) into vfill (the slots K(t-1) and V(t-2)
+  // left two barriers earlier) and waits only for the copies of the previous VALU phase,
+  // K(t+1) and V(t), which the next MFMA phase reads: each copy has two and a half phases
+  // to land.
+  auto phase_pair = [&](auto copier_c, int t, const char* kcur, const char* vprev, char* knext,
+                        char* vfill) __attribute__((always_inline)) {
+    constexpr bool COPIER = decltype(copier_c)::value;
     // Uniform MFMA phase: at t = 0 the probabilities are zero; at t = nt the scores come
-    // from stale (finite) K data and are never used.
+    // from stale K data (or an unwritten slot) and are never used.
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);  // MFMA phase first at the SIMD's issue arbiter
     mfma_run<D, 0, Pairs<D>::NPV + Pairs<D>::NQK>(vprev, kcur, p2, qop, oacc, s0, s1, j, half);
-    __syncthreads();
-    if (!isB && t < nt)
-      tile_copy<D, 4>(t + 1 < nt ? kg + (long)(t + 1) * 64 * D : nullptr, N - (t + 1) * 64, knext,
-                      vg + (long)t * 64, Np, vfill, wq, lane);
+    __builtin_amdgcn_s_setprio(0);
+    barrier_nofence();
+    // Always 8 copy instructions, so the wait below is one fixed count: a tile past the
+    // end gets a zero-length descriptor (no memory access) into a slot nobody reads again.
+    if constexpr (COPIER)
+      tile_copy<D, 4>(coff, kg + (long)(t + 2) * 64 * D, N - (t + 2) * 64, knext, vg + (long)(t + 1) * 64, Np,
+                      t + 1 < nt ? vbytes - (uint32_t)(t + 1) * 128 : 0u, vfill, wq);
     if (t < nt) {
       if ((t + 1) * 64 > N) {  // ragged last tile: keys >= N do not exist
 #pragma unroll
@@ -119,16 +139,26 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       softmax_tile<DB>(s0, s1, sl2, m, l, oacc, p2);
     }
-    if (!isB) wait_tile_copies();
-    __syncthreads();
+    if constexpr (COPIER) wait_tile_copies_keep<KP + VP>();  // K(t+1), V(t) landed; K(t+2), V(t+1) may fly
+    barrier_nofence();
   };
-  // tiles alternate between the two K slots and the two V slots; unrolled by two so
-  // every LDS array is named statically (keeps the compiler's LDS alias tracking exact)
-  for (int t = 0; t <= nt; t += 2) {
-    phase_pair(t, kt0, vt1, kt1, vt0);
-    if (t + 1 <= nt) phase_pair(t + 1, kt1, vt0, kt0, vt1);
+  // unrolled by three so every LDS array is named statically, and instantiated once per half
+  // (copier or not) so the compiler tracks the copies on straight-line paths
+  auto tile_loop = [&](auto copier_c) __attribute__((always_inline)) {
+    for (int t = 0; t <= nt; t += 3) {
+      phase_pair(copier_c, t, kt0, vt2, kt2, vt1);
+      if (t + 1 <= nt) {  // nested, so every path into a phase passes the previous phase's wait
+        phase_pair(copier_c, t + 1, kt1, vt0, kt0, vt2);
+        if (t + 2 <= nt) phase_pair(copier_c, t + 2, kt2, vt1, kt1, vt0);
+      }
+    }
+  };
+  if (!isB) tile_loop(std::true_type());
+  else tile_loop(std::false_type());
+  if (!isB) {
+    wait_tile_copies();  // no copy may still be writing LDS when the workgroup ends
+    barrier_nofence();   // same barrier count in both halves
   }
-  if (!isB) __syncthreads();  // same barrier count in both halves
 
   const float lse_row = finish_store<DB>(oacc, m, l, qrow < N ? o + (base + qrow) * D : nullptr, half);
   if (lse && qrow < N && half == 0) lse[base + qrow] = lse_row;

@@ -218,7 +218,8 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   constexpr int DB = D / 32, NPV = Pairs<D>::NPV, NQK = Pairs<D>::NQK;
   __shared__ __align__(16) char ks[Swz<D>::KB];
   __shared__ __align__(16) char vs[Swz<D>::VB];
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, j = lane % 32, half = lane / 32;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, j = lane % 32,
+            half = lane / 32;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / g.C, c = item % g.C;
   const long cube_base = (long)bh * g.C;
@@ -241,14 +242,16 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   bf16x2 p2[16];
 
   int cur = plan[0];
-  tile_copy<D, 2>(kc + (cube_base + cur) * 64 * D, 64, ks, vct + (cube_base + cur) * D * 64, 64, vs, wave, lane);
+  const CopyOffsets<D, 2> coff(wave, lane, 64);
+  constexpr uint32_t CUBE_BYTES = 64u * D * 2;
+  tile_copy<D, 2>(coff, kc + (cube_base + cur) * 64 * D, 64, ks, vct + (cube_base + cur) * D * 64, 64, CUBE_BYTES, vs, wave);
   for (int t = 0; t < k; ++t) {
     wait_tile_copies();  // V(t) (and, at t = 0, K(t)) landed
     __syncthreads();
     mfma_run<D, NPV, NPV + NQK>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
     __syncthreads();                                                       // K slot free
     const int nxt = t + 1 < k ? plan[t + 1] : -1;
-    if (nxt >= 0) tile_copy<D, 2>(kc + (cube_base + nxt) * 64 * D, 64, ks, nullptr, 0, nullptr, wave, lane);
+    if (nxt >= 0) tile_copy<D, 2>(coff, kc + (cube_base + nxt) * 64 * D, 64, ks, nullptr, 0, 0, nullptr, wave);
     int kt, kh, kw;
     cube_coords(g, cur, kt, kh, kw);
     const int lt = g.T - 4 * kt, lh = g.H - 4 * kh, lw = g.W - 4 * kw;
@@ -265,7 +268,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     wait_tile_copies();                                            // K(t+1) landed
     __syncthreads();                                               // V slot free, K(t+1) visible
     if (nxt >= 0)
-      tile_copy<D, 2>(nullptr, 0, nullptr, vct + (cube_base + nxt) * D * 64, 64, vs, wave, lane);
+      tile_copy<D, 2>(coff, nullptr, 0, nullptr, vct + (cube_base + nxt) * D * 64, 64, CUBE_BYTES, vs, wave);
     cur = nxt;
   }
   int ct, ch, cw;

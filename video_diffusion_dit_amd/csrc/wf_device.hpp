@@ -65,6 +65,26 @@ __device__ __forceinline__ void wait_tile_copies() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's global->LDS copies landed
 }
 
+// Workgroup barrier without __syncthreads' memory fence, whose release half
+// would drain every outstanding global->LDS copy (vmcnt(0)).  The asm memory
+// clobbers keep the compiler from moving LDS accesses across it; the hardware
+// ordering it needs is explicit: LDS operand reads are consumed (waited) before
+// a phase ends, and copies are waited with vmcnt before the barrier that
+// publishes them.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// vmcnt(KEEP): every global->LDS copy of this wavefront except the KEEP most
+// recently issued has landed (loads retire in issue order for this counter).
+template <int KEEP>
+__device__ __forceinline__ void wait_tile_copies_keep() {
+  static_assert(KEEP >= 0 && KEEP < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | KEEP);
+}
+
 struct P4 {
   bf16x2 v[4];
 };
@@ -85,35 +105,67 @@ struct Swz {
   __host__ __device__ static constexpr int vslot(int d, int c) { return c ^ ((d >> 1) & 7); }
 };
 
-// NWC wavefronts (w = 0..NWC-1) copy one K tile and/or one V^T tile global ->
-// LDS with global_load_lds_dwordx4 (each instruction lays 64 lanes x 16 bytes
-// contiguously at a wave-uniform LDS address).  K rows >= krows are not read:
-// row krows-1 is fetched in their place and those keys are masked later.
-// kg / vg may be null to skip that tile.  V^T row d starts at vg + d * vld.
+// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes
+// return zero instead of touching memory (gfx9 range check on the VGPR offset).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Global->LDS tile copies.  Wavefront w of NWC copies K pieces g = i * NWC + w
+// (i < KPW), each 1 KiB of the K tile's LDS image: lane L fetches the 16-byte
+// chunk that belongs at LDS byte g * 1024 + 16 L under the K swizzle.  The
+// swizzle depends on the row only through r & 15, so the lane's global offset
+// repeats with period KPER pieces up to a uniform step of KPER * NWC KiB; V^T
+// pieces likewise repeat every piece up to a uniform step of NWC * 8 rows.
+// Only KPER + 1 per-lane offsets are kept in registers.
 template <int D, int NWC>
-__device__ __forceinline__ void tile_copy(const uint16_t* __restrict__ kg, int krows, char* kdst,
-                                          const uint16_t* __restrict__ vg, long vld, char* vdst, int w,
-                                          int lane) {
-  constexpr int KPIECES = Swz<D>::KB / 1024, VPIECES = Swz<D>::VB / 1024, CPR = Swz<D>::KCPR;
-  static_assert(KPIECES % NWC == 0 && VPIECES % NWC == 0, "pieces per wavefront");
-  if (kg) {
+struct CopyOffsets {
+  static constexpr int CPR = Swz<D>::KCPR, RPP = 64 / CPR;  // 16-byte chunks per K row, K rows per piece
+  static constexpr int KPW = Swz<D>::KB / 1024 / NWC, VPW = Swz<D>::VB / 1024 / NWC;
+  static constexpr int KPER = (NWC * RPP) % 16 == 0 ? 1 : (2 * NWC * RPP) % 16 == 0 ? 2 : 4;
+  static_assert(KPW % KPER == 0, "pieces per wavefront");
+  static_assert((NWC * 8) % 16 == 0, "V^T swizzle must repeat every piece");
+  uint32_t k[KPER], v;
+  __device__ __forceinline__ CopyOffsets(int w, int lane, int vld) {
 #pragma unroll
-    for (int i = 0; i < KPIECES / NWC; ++i) {
-      const int g = i * NWC + w, P = g * 64 + lane;
-      const int r = P / CPR, c = Swz<D>::kslot(r, P % CPR);  // the swizzle is an involution in c
-      const int rr = min(r, krows - 1);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kg + (long)rr * D + c * 8),
-                                       (__attribute__((address_space(3))) void*)(kdst + g * 1024), 16, 0, 0);
+    for (int i = 0; i < KPER; ++i) {
+      const int P = (i * NWC + w) * 64 + lane, r = P / CPR, c = Swz<D>::kslot(r, P % CPR);
+      k[i] = (uint32_t)(r * D * 2 + c * 16);
+    }
+    const int d = w * 8 + lane / 8, c = Swz<D>::vslot(d, lane % 8);
+    v = (uint32_t)(d * vld * 2 + c * 16);
+  }
+};
+
+// Copy one K tile (rows [0, krows) exist; the rest are not read and land as
+// zero or stay stale, both harmless since those keys are masked) and/or one
+// V^T tile (row stride vld elements, vbytes bytes addressable from vg) into
+// LDS with buffer_load ... lds.  kg / vg point at the tiles' first elements;
+// null skips that tile.  Every access is range-checked by the buffer
+// descriptor against the extent given.
+template <int D, int NWC>
+__device__ __forceinline__ void tile_copy(const CopyOffsets<D, NWC>& off, const uint16_t* kg, int krows,
+                                          char* kdst, const uint16_t* vg, int vld, uint32_t vbytes, char* vdst,
+                                          int w) {
+  using CO = CopyOffsets<D, NWC>;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  constexpr int KSTEP = CO::KPER * NWC * 1024;  // global bytes between pieces i and i + KPER
+  if (kg) {  // one descriptor per KPER-piece step, bounded at row krows (scalar work only)
+#pragma unroll
+    for (int i = 0; i < CO::KPW; ++i) {
+      const int base = (i / CO::KPER) * KSTEP, left = krows * D * 2 - base;
+      const uint32_t bytes = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : min(left, KSTEP));  // keep it scalar
+      const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(reinterpret_cast<const char*>(kg) + base, bytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kdst + (i * NWC + w) * 1024), 16,
+                                               (int)off.k[i % CO::KPER], 0, 0, 0);
     }
   }
   if (vg) {
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg, vbytes);
 #pragma unroll
-    for (int i = 0; i < VPIECES / NWC; ++i) {
-      const int g = i * NWC + w, P = g * 64 + lane;
-      const int d = P / 8, c = Swz<D>::vslot(d, P % 8);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vg + (long)d * vld + c * 8),
-                                       (__attribute__((address_space(3))) void*)(vdst + g * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < CO::VPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vdst + (i * NWC + w) * 1024), 16, (int)off.v,
+                                               i * NWC * 8 * vld * 2, 0, 0);
   }
 }
 
@@ -127,15 +179,32 @@ struct Pairs {
   static constexpr int NQK = 2 * (D / 16);
 };
 
+// Per-lane LDS byte offsets of the MFMA operand reads.  With c = 2 s + half
+// (s = k-step) the swizzled chunk is (2 s + half) ^ f(row) = 2 s ^ (half ^ f(row)),
+// and the row's byte offset has zero bits where the chunk lives, so every
+// operand address is one per-lane base XOR 32 s plus an immediate (the tile,
+// and the 32-row block).  The bases are made opaque once per run so the
+// compiler computes the XORs in place instead of keeping one register per
+// k-step alive across the loop.
 template <int D>
-__device__ __forceinline__ uint4 mfma_operand(int i, const char* vt, const char* kt, int j, int half) {
-  constexpr int NPV = Pairs<D>::NPV;
-  if (i < NPV) {  // ks = i / (D/32), block b = i % (D/32)
-    const int ks = i / (D / 32), b = i % (D / 32), d = b * 32 + j, c = ks * 2 + half;
-    return *reinterpret_cast<const uint4*>(vt + d * 128 + Swz<D>::vslot(d, c) * 16);
+struct OperandBase {
+  uint32_t k, v;
+  __device__ __forceinline__ OperandBase(int j, int half) {
+    const int kf = Swz<D>::KCPR == 16 ? (j & 15) : ((j >> 1) & 7);
+    k = (uint32_t)(j * D * 2 + 16 * (half ^ kf));
+    v = (uint32_t)(j * 128 + 16 * (half ^ ((j >> 1) & 7)));
   }
-  const int kk = (i - NPV) / 2, r = ((i - NPV) % 2) * 32 + j, c = kk * 2 + half;
-  return *reinterpret_cast<const uint4*>(kt + r * (D * 2) + Swz<D>::kslot(r, c) * 16);
+};
+
+template <int D>
+__device__ __forceinline__ uint4 mfma_operand(int i, const char* vt, const char* kt, const OperandBase<D>& ob) {
+  constexpr int NPV = Pairs<D>::NPV;
+  if (i < NPV) {  // ks = i / (D/32), block b = i % (D/32): V^T rows b*32 + j
+    const int ks = i / (D / 32), b = i % (D / 32);
+    return *reinterpret_cast<const uint4*>(vt + b * 32 * 128 + (ob.v ^ (uint32_t)(32 * ks)));
+  }
+  const int kk = (i - NPV) / 2, kb = (i - NPV) % 2;  // K rows kb*32 + j
+  return *reinterpret_cast<const uint4*>(kt + kb * 32 * D * 2 + (ob.k ^ (uint32_t)(32 * kk)));
 }
 
 template <int D>
@@ -167,13 +236,15 @@ __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const b
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
   }
+  OperandBase<D> ob(j, half);
+  asm volatile("" : "+v"(ob.k), "+v"(ob.v));
   uint4 ring[R];
 #pragma unroll
-  for (int u = 0; u < PF && u < NP; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, j, half);
+  for (int u = 0; u < PF && u < NP; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, ob);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    if (i + PF < NP) ring[(i + PF) % R] = mfma_operand<D>(I0 + i + PF, vt, kt, j, half);
+    if (i + PF < NP) ring[(i + PF) % R] = mfma_operand<D>(I0 + i + PF, vt, kt, ob);
     mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
     __builtin_amdgcn_sched_barrier(0);
   }
