@@ -139,3 +139,18 @@ def test_dense_full_shape_sampled(wf, name, heads):
     ref_all = oracle_heads(wl, q, k, v, allh, few)
     for bh in allh:
         assert_close(o[bh][few], ref_all[bh][0], f"O b{bh[0]} h{bh[1]} 3 rows")
+
+
+def test_dense_long_ragged_sampled(wf):
+    """One head of 1,044,735 tokens (grid 17 x 241 x 255, ragged last tile): 32-bit
+    offsets and buffer extents far beyond the benchmark shapes, sampled rows."""
+    wl = synth.small_workload("long", 1, 1, 17, 241, 255, 128, structured=True, seed=41)
+    log(f"dense long N={wl.N} D={wl.D} (sampled rows)")
+    q, k, v = synth.make_qkv(wl)
+    o, lse = run_dense(wf, q, k, v)
+    rows = sample_rows(wl.N, np.random.default_rng(wl.seed), n_random=24)
+    ref_o, ref_l = oracle.attention(synth.bits_to_f64(q[0, 0]), synth.bits_to_f64(k[0, 0]),
+                                    synth.bits_to_f64(v[0, 0]), wl.scale, rows)
+    assert_close(o[0, 0][rows], ref_o, f"O ({rows.size} rows)")
+    assert errors(lse[0, 0][rows], ref_l)[0] <= LSE_MAX_ABS
+    assert np.isfinite(o).all()

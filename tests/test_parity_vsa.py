@@ -169,6 +169,26 @@ def test_vsa_720p_full(wf):
     check_fine(wl, q, k, v, g, tok, [(0, 3), (1, 36)], cubes)
 
 
+def test_vsa_max_cubes(wf):
+    """The largest supported plan: 4,096 cubes (16 x 16 x 16, every axis padded), top-64.
+
+    Exercises the widest top-k path (more than 2,048 cubes per row) and the
+    fine stage's 32-bit offsets at the cube limit.
+    """
+    wl = synth.small_workload("vsa_max", 1, 1, 61, 62, 63, 128, structured=True, seed=40, topk=64)
+    log(f"vsa max cubes grid {wl.T}x{wl.H}x{wl.W} N={wl.N} topk={wl.topk}")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    heads = [(0, 0)]
+    ref, tok = coarse_ref(wl, q, k, heads, wl.topk)
+    assert tok.shape[0] == 4096
+    check_scores_and_idx(g, ref, heads)
+    assert np.isfinite(g["o"]).all()
+    cubes = sorted(set([0, 15, 16, 255, 256, 2047, 2048, 4080, 4095] +
+                       np.random.default_rng(40).choice(4096, 11, replace=False).tolist()))
+    check_fine(wl, q, k, v, g, tok, heads, cubes)
+
+
 def test_vsa_fine_caller_plan_and_validation(wf, monkeypatch):
     """A caller-supplied plan runs as given; with WF_VALIDATE=1 a bad plan is refused."""
     import torch

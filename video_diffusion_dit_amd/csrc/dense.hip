@@ -51,9 +51,10 @@ __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict
 // (at raised issue priority) while the other is in its VALU phase.  K and V^T
 // tiles rotate through three LDS slots each: in its VALU phase t half A copies
 // K(t+2) and V(t+1) global -> LDS with buffer loads (no staging registers)
-// into the slots K(t-1) and V(t-2) left, and waits only for the previous
-// phase's copies, so each copy has about two phases to land.  Within an MFMA
-// phase the LDS operand reads run four MFMAs ahead of use.
+// into the slots K(t-1) and V(t-2) left, and waits for them at the end of its
+// next MFMA phase, so each copy has a phase to land.  Within an MFMA phase the
+// LDS operand reads run four MFMAs ahead of use; the first four are read at the
+// end of the wavefront's VALU phase, before the barrier.
 template <int D>
 __global__ void __launch_bounds__(512, 1)
 wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -99,7 +100,7 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   constexpr int KP = Swz<D>::KB / 1024 / 4, VP = Swz<D>::VB / 1024 / 4;  // copies per wavefront of half A
   const int nt = (N + 63) / 64;
   // Three K slots and three V slots: tile t's K sits in slot t % 3, its V in slot t % 3.
-  // Prologue: K(0), then K(1) and V(0); K(0) must land before the first MFMA phase.
+  // Prologue: K(0), K(1) and V(0).
   const CopyOffsets<D, 4> coff(wq, lane, Np);
   const uint32_t vbytes = (uint32_t)D * Np * 2;  // one head's V^T
   if (!isB) {
@@ -114,18 +115,24 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // left two barriers earlier) and waits only for the copies of the previous VALU phase,
   // K(t+1) and V(t), which the next MFMA phase reads: each copy has two and a half phases
   // to land.
-  auto phase_pair = [&](auto copier_c, int t, const char* kcur, const char* vprev, char* knext,
-                        char* vfill) __attribute__((always_inline)) {
+  // The first operands of every MFMA phase are read at the end of the wavefront's previous
+  // VALU phase, before the barrier, so the matrix pipe does not idle through the LDS latency
+  // at each phase start.  Those operands are V(t-1) rows, so V(t-1) must be in LDS one phase
+  // before its MFMA phase: half A waits for the copies of its VALU phase t at the end of its
+  // MFMA phase t+1 (one phase of latency), which publishes K(t+2) and V(t+1) from phase 2t+3
+  // on; both are first read in phase 2t+4 (V(t+1) by the prefetch at the end of 2t+3).
+  uint4 ring[kRing];
+  auto phase_pair = [&](auto copier_c, int t, const char* kcur, const char* vprev, char* knext, char* vfill,
+                        const char* vnext) __attribute__((always_inline)) {
     constexpr bool COPIER = decltype(copier_c)::value;
-    // Uniform MFMA phase: at t = 0 the probabilities are zero; at t = nt the scores come
-    // from stale K data (or an unwritten slot) and are never used.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);  // MFMA phase first at the SIMD's issue arbiter
-    mfma_run<D, 0, Pairs<D>::NPV + Pairs<D>::NQK>(vprev, kcur, p2, qop, oacc, s0, s1, j, half);
+    mfma_run<D, 0, Pairs<D>::NPV + Pairs<D>::NQK, true>(vprev, kcur, p2, qop, oacc, s0, s1, j, half, ring);
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (COPIER) wait_tile_copies();  // K(t+1), V(t) landed
     barrier_nofence();
-    // Always 8 copy instructions, so the wait below is one fixed count: a tile past the
-    // end gets a zero-length descriptor (no memory access) into a slot nobody reads again.
+    // Always 8 copy instructions: a tile past the end gets a zero-length descriptor (no
+    // memory access) into a slot nobody reads again.
     if constexpr (COPIER)
       tile_copy<D, 4>(coff, kg + (long)(t + 2) * 64 * D, N - (t + 2) * 64, knext, vg + (long)(t + 1) * 64, Np,
                       t + 1 < nt ? vbytes - (uint32_t)(t + 1) * 128 : 0u, vfill, wq);
@@ -139,17 +146,18 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       softmax_tile<DB>(s0, s1, sl2, m, l, oacc, p2);
     }
-    if constexpr (COPIER) wait_tile_copies_keep<KP + VP>();  // K(t+1), V(t) landed; K(t+2), V(t+1) may fly
+    mfma_prefill<D, 0>(ring, vnext, kcur, j, half);  // first operands of MFMA phase t+1: V(t) rows
     barrier_nofence();
   };
   // unrolled by three so every LDS array is named statically, and instantiated once per half
   // (copier or not) so the compiler tracks the copies on straight-line paths
   auto tile_loop = [&](auto copier_c) __attribute__((always_inline)) {
+    mfma_prefill<D, 0>(ring, vt2, kt0, j, half);  // MFMA phase 0: V(-1), the zero slot
     for (int t = 0; t <= nt; t += 3) {
-      phase_pair(copier_c, t, kt0, vt2, kt2, vt1);
+      phase_pair(copier_c, t, kt0, vt2, kt2, vt1, vt0);
       if (t + 1 <= nt) {  // nested, so every path into a phase passes the previous phase's wait
-        phase_pair(copier_c, t + 1, kt1, vt0, kt0, vt2);
-        if (t + 2 <= nt) phase_pair(copier_c, t + 2, kt2, vt1, kt1, vt0);
+        phase_pair(copier_c, t + 1, kt1, vt0, kt0, vt2, vt1);
+        if (t + 2 <= nt) phase_pair(copier_c, t + 2, kt2, vt1, kt1, vt0, vt2);
       }
     }
   };

@@ -227,20 +227,35 @@ __device__ __forceinline__ void mfma_pair(int i, uint4 a, const bf16x2* p2, cons
 // them; each step is fenced with sched_barrier so the compiler keeps that
 // distance (it otherwise reads each operand right before its MFMA and the LDS
 // latency stalls the matrix pipe).  Scores are zeroed first if the run
-// contains K Q^T pairs.
-template <int D, int I0, int I1>
+// contains K Q^T pairs.  The ring belongs to the caller: with PREFILLED its
+// first PF entries were already read by mfma_prefill (e.g. before a barrier,
+// so the run starts its first MFMA without waiting for LDS).
+constexpr int kRingPF = 4, kRing = kRingPF + 1;
+
+template <int D, int I0>
+__device__ __forceinline__ void mfma_prefill(uint4 (&ring)[kRing], const char* vt, const char* kt, int j, int half) {
+  OperandBase<D> ob(j, half);
+  asm volatile("" : "+v"(ob.k), "+v"(ob.v));
+#pragma unroll
+  for (int u = 0; u < kRingPF; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, ob);
+}
+
+template <int D, int I0, int I1, bool PREFILLED = false>
 __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
-                                         f32x16* o, f32x16& s0, f32x16& s1, int j, int half) {
-  constexpr int PF = 4, R = PF + 1, NP = I1 - I0;
+                                         f32x16* o, f32x16& s0, f32x16& s1, int j, int half,
+                                         uint4 (&ring)[kRing]) {
+  constexpr int PF = kRingPF, R = kRing, NP = I1 - I0;
+  static_assert(NP >= PF, "run shorter than the prefetch distance");
   if constexpr (I1 > Pairs<D>::NPV) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
   }
   OperandBase<D> ob(j, half);
   asm volatile("" : "+v"(ob.k), "+v"(ob.v));
-  uint4 ring[R];
+  if constexpr (!PREFILLED) {
 #pragma unroll
-  for (int u = 0; u < PF && u < NP; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, ob);
+    for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, ob);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -248,6 +263,13 @@ __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const b
     mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+template <int D, int I0, int I1>
+__device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
+                                         f32x16* o, f32x16& s0, f32x16& s1, int j, int half) {
+  uint4 ring[kRing];
+  mfma_run<D, I0, I1, false>(vt, kt, p2, qop, o, s0, s1, j, half, ring);
 }
 
 // ------------------------------------------------------------- softmax tile
