@@ -206,10 +206,11 @@ __global__ void __launch_bounds__(256) wf_vsa_topk(const float* __restrict__ s,
 // current cube sit in one K slot and one V slot of LDS (32 KiB, so several
 // workgroups share a CU and hide each other's latency).  The slots have
 // separate lifetimes: the copy of the next K cube starts as soon as both
-// wavefronts have their scores, the copy of the next V cube as soon as both
-// have accumulated P V; each copy lands behind the other half of the tile's
-// work.  Padded key slots of edge cubes are masked; output rows are scattered
-// back to grid order, padded query slots are not written.
+// wavefronts have their scores and is waited for at the next tile's start; the
+// copy of the next V cube starts once both have accumulated P V and is waited
+// for only before the next P V, so it lands behind the next tile's scores and
+// softmax.  Padded key slots of edge cubes are masked; output rows are
+// scattered back to grid order, padded query slots are not written.
 template <int D>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
@@ -244,14 +245,16 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   int cur = plan[0];
   const CopyOffsets<D, 2> coff(wave, lane, 64);
   constexpr uint32_t CUBE_BYTES = 64u * D * 2;
-  tile_copy<D, 2>(coff, kc + (cube_base + cur) * 64 * D, 64, ks, vct + (cube_base + cur) * D * 64, 64, CUBE_BYTES, vs, wave);
+  constexpr int KP = CopyOffsets<D, 2>::KPW, VP = CopyOffsets<D, 2>::VPW;  // copies per wavefront and tile
+  tile_copy<D, 2>(coff, kc + (cube_base + cur) * 64 * D, 64, ks, nullptr, 0, 0, nullptr, wave);
+  tile_copy<D, 2>(coff, nullptr, 0, nullptr, vct + (cube_base + cur) * D * 64, 64, CUBE_BYTES, vs, wave);
+  wait_tile_copies_keep<VP>();  // K(0) landed; V(0) may still fly
   for (int t = 0; t < k; ++t) {
-    wait_tile_copies();  // V(t) (and, at t = 0, K(t)) landed
-    __syncthreads();
+    barrier_nofence();  // K(t) visible
     mfma_run<D, NPV, NPV + NQK>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
-    __syncthreads();                                                       // K slot free
-    const int nxt = t + 1 < k ? plan[t + 1] : -1;
-    if (nxt >= 0) tile_copy<D, 2>(coff, kc + (cube_base + nxt) * 64 * D, 64, ks, nullptr, 0, 0, nullptr, wave);
+    barrier_nofence();                                                     // K slot free
+    const int nxt = t + 1 < k ? plan[t + 1] : cur;  // past the end: a harmless copy of the last cube
+    tile_copy<D, 2>(coff, kc + (cube_base + nxt) * 64 * D, 64, ks, nullptr, 0, 0, nullptr, wave);
     int kt, kh, kw;
     cube_coords(g, cur, kt, kh, kw);
     const int lt = g.T - 4 * kt, lh = g.H - 4 * kh, lw = g.W - 4 * kw;
@@ -264,13 +267,15 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
       }
     }
     softmax_tile<DB>(s0, s1, sl2, m, l, oacc, p2);
+    wait_tile_copies_keep<KP>();  // V(t) landed (it had the scores and the softmax to do so); K(t+1) may fly
+    barrier_nofence();            // V(t) visible
     mfma_run<D, 0, NPV>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // O += P V(t)
-    wait_tile_copies();                                            // K(t+1) landed
-    __syncthreads();                                               // V slot free, K(t+1) visible
-    if (nxt >= 0)
-      tile_copy<D, 2>(coff, nullptr, 0, nullptr, vct + (cube_base + nxt) * D * 64, 64, CUBE_BYTES, vs, wave);
+    barrier_nofence();                                             // V slot free
+    tile_copy<D, 2>(coff, nullptr, 0, nullptr, vct + (cube_base + nxt) * D * 64, 64, CUBE_BYTES, vs, wave);
+    wait_tile_copies_keep<VP>();  // K(t+1) landed; V(t+1) may fly
     cur = nxt;
   }
+  wait_tile_copies();  // no copy may still be writing LDS when the workgroup ends
   int ct, ch, cw;
   cube_coords(g, c, ct, ch, cw);
   const int tok = slot_token(g, ct, ch, cw, slot);
