@@ -119,6 +119,22 @@ def test_dense_large_logits_stay_finite(wf):
     assert_close(o[0, 0], ref_o, "O adversarial")
 
 
+def test_dense_d64_multi_tile_sampled(wf):
+    """Head dimension 64 over several query tiles of 256 rows and a ragged key tail
+    (grid 9 x 23 x 31 = 6,417 tokens), 2 x 6 heads: every head sampled."""
+    wl = synth.small_workload("d64", 2, 6, 9, 23, 31, 64, structured=True, seed=64)
+    log(f"dense d64 B={wl.B} Hh={wl.Hh} N={wl.N} D={wl.D} (sampled rows of every head)")
+    q, k, v = synth.make_qkv(wl)
+    o, lse = run_dense(wf, q, k, v)
+    rows = sample_rows(wl.N, np.random.default_rng(wl.seed), n_random=64)
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.Hh)]
+    ref = oracle_heads(wl, q, k, v, heads, rows)
+    for bh in heads:
+        assert_close(o[bh][rows], ref[bh][0], f"O b{bh[0]} h{bh[1]} ({rows.size} rows)")
+        assert errors(lse[bh][rows], ref[bh][1])[0] <= LSE_MAX_ABS
+    assert np.isfinite(o).all()
+
+
 @pytest.mark.parametrize("name,heads", [("dense_480p_12h", [(0, 0), (0, 5), (0, 11)]),
                                         ("dense_480p_cfg", [(0, 0), (0, 39), (1, 7), (1, 22)]),
                                         ("dense_720p_cfg", [(0, 1), (1, 30)])])
