@@ -160,7 +160,7 @@ def main():
         summarize(args.summarize)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
+        print(json.dumps({"error": "bench.py times one GPU (one GPU's share of the heads): --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import numpy as np

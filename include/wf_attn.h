@@ -48,7 +48,7 @@ extern "C" {
 typedef enum wf_status {
   WF_OK = 0,
   WF_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, bad size, non-finite scale */
-  WF_ERR_UNSUPPORTED = 2,  /* a head dimension or size this build does not handle */
+  WF_ERR_UNSUPPORTED = 2,  /* a head dimension or size the library does not handle */
   WF_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes query */
   WF_ERR_BAD_INDEX = 4,    /* a top-k plan that is out of range or not strictly ascending */
   WF_ERR_HIP = 5           /* the HIP runtime reported an error */
