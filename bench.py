@@ -6,7 +6,9 @@ in HBM:
   * VSA, 1 x 40 heads, grid 21x30x52 padded to 624 cubes, top-32: the coarse
     call (gather + pool, scores, top-k) and the fine call.
 Prints one JSON line.  The per-kernel times come from HIP events the library
-records on the launch stream around each kernel.
+records on the launch stream around each kernel.  After the timed steps two
+extra records are taken (not part of the step): VSA at top-78, and the step's
+kernels on one GPU's share of the heads when eight GPUs split them.
 """
 from __future__ import annotations
 
@@ -26,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+PEAK_CLOCK_GHZ = 2.4        # engine clock the published MFMA peak assumes
 DENSE = "dense_480p_cfg"
 VSA = "vsa_480p"
 # HBM traffic of the dense kernel, measured with rocprofv3 FETCH_SIZE / WRITE_SIZE; used only while
@@ -42,23 +45,28 @@ def sources_sha256(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """Bytes per launch of wf_dense_fwd from the committed counter summary, or None if stale."""
+def measured_counters():
+    """The committed rocprofv3 counter summary of wf_dense_fwd, or {} if missing or stale."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("source_sha256") != sources_sha256(DENSE_SOURCES):
-        return None
-    return t.get("bytes_per_launch")
+        return {}
+    return t
+
+
+def measured_traffic():
+    """Bytes per launch of wf_dense_fwd from the committed counter summary, or None if stale."""
+    return measured_counters().get("bytes_per_launch")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (used for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -66,8 +74,8 @@ def parse():
     p.add_argument("--summarize", metavar="ROCPROF_DIR", default=None,
                    help="print a text summary of rocprofv3 CSV output under ROCPROF_DIR and exit")
     p.add_argument("--no-extra", action="store_true",
-                   help="skip the top-78 VSA record after the timed steps (profiling runs: keeps "
-                        "per-kernel averages to the step's own launches)")
+                   help="skip the extra records after the timed steps (VSA top-78, one GPU's share of "
+                        "heads); profiling runs use it to keep per-kernel averages to the step's own launches")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB (a known-size "
                         "kernel that calibrates the profiler's HBM byte counters)")
@@ -242,6 +250,43 @@ def main():
             k78_ms[name] = tot / n
         wf.profile_enable(False)
 
+    # extra record (not part of the step): one GPU's share of the heads when 8 GPUs split them
+    # (5 of 40 per CFG branch): the same kernels at Hh = 5 and full N
+    share = None
+    if not args.no_extra:
+        hs = wd.Hh // 8
+        qs, ks_, vs_ = (x[:, :hs].contiguous() for x in (qd, kd, vd))
+        os_ = torch.empty((wd.B, hs, wd.N, wd.D), dtype=torch.float32, device=dev)
+        ws_s = torch.empty(wf.dense_workspace_bytes(wd.B, hs, wd.N, wd.D), dtype=torch.uint8, device=dev)
+        qvs, kvs, vvs = (x[:, :hs].contiguous() for x in (qv, kv, vv))
+        ovs = torch.empty((wv.B, hs, wv.N, wv.D), dtype=torch.float32, device=dev)
+        idxs = torch.empty((wv.B, hs, C, wv.topk), dtype=torch.int32, device=dev)
+        ws_vs = torch.empty(wf.vsa_workspace_bytes(wv.B, hs, wv.T, wv.H, wv.W, wv.D), dtype=torch.uint8, device=dev)
+
+        def step_share():
+            wf.wf_attn_dense(qs, ks_, vs_, out=os_, workspace=ws_s)
+            wf.wf_vsa_coarse_topk(qvs, kvs, vvs, grid, wv.topk, idx=idxs, workspace=ws_vs)
+            wf.wf_vsa_fine(ws_vs, idxs, (wv.B, hs, wv.N, wv.D), grid, out=ovs)
+
+        for _ in range(3):
+            step_share()
+        torch.cuda.synchronize()
+        wf.profile_enable(True)
+        for _ in range(10):
+            step_share()
+        torch.cuda.synchronize()
+        sk = {}
+        for name in ("wf_transpose_v", "wf_dense_fwd", "wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine"):
+            n, tot = wf.profile_query(name)
+            sk[name] = tot / n
+        wf.profile_enable(False)
+        sd = sk["wf_transpose_v"] + sk["wf_dense_fwd"]
+        share = {"heads": hs, "of_gpus": 8,
+                 "dense_ms_per_call": sd,
+                 "dense_tflops_kernel": 4.0 * wd.B * hs * wd.N * wd.N * wd.D / (sk["wf_dense_fwd"] * 1e-3) / 1e12,
+                 "vsa_ms_per_call": sk["wf_vsa_gather"] + sk["wf_vsa_scores"] + sk["wf_vsa_topk"] + sk["wf_vsa_fine"],
+                 "kernel_ms": sk}
+
     fl_d = dense_flops(wd)
     fl_v = vsa_flops(wv, C)
     by_v = vsa_bytes(wv, C)
@@ -250,6 +295,7 @@ def main():
     dense_tf = fl_d / (kern["wf_dense_fwd"] * 1e-3) / 1e12
     # dense attention at the VSA call's own shape (B=1, 40 heads) is half the CFG-pair call
     ms_dense_same = ms_dense * wv.B / wd.B
+    counters = measured_counters()
     out = {
         "metric": "attention TFLOP/s and ms/call at 32,760 tok x 40 heads x d128 (dense, VSA)",
         "value": (fl_d + fl_v["total"]) / (ms_step * 1e-3) / 1e12,
@@ -281,6 +327,9 @@ def main():
             "traffic": measured_traffic(),
         },
         "dense": {
+            "profiled_clock_ghz": counters.get("clock_ghz"),
+            "frac_peak_at_profiled_clock": (dense_tf / (PEAK_BF16_TFLOPS * counters["clock_ghz"] / PEAK_CLOCK_GHZ)
+                                            if counters.get("clock_ghz") else None),
             "ms_per_call": ms_dense,
             "kernel_ms": {"wf_transpose_v": kern["wf_transpose_v"], "wf_dense_fwd": kern["wf_dense_fwd"]},
             "tflops_call": fl_d / (ms_dense * 1e-3) / 1e12,
@@ -292,9 +341,12 @@ def main():
             "ms_per_call": ms_vsa,
             "kernel_ms": {k: kern[k] for k in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine")},
             "fine_tflops": fl_v["fine"] / (kern["wf_vsa_fine"] * 1e-3) / 1e12,
+            "fine_tflops_padded_queries": fl_v["fine"] * C * 64 / wv.N / (kern["wf_vsa_fine"] * 1e-3) / 1e12,
             "fine_frac_bf16_peak": fl_v["fine"] / (kern["wf_vsa_fine"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "gather_gbs": by_v["gather"] / (kern["wf_vsa_gather"] * 1e-3) / 1e9,
             "topk_gbs": by_v["topk"] / (kern["wf_vsa_topk"] * 1e-3) / 1e9,
+            "gather_frac_hbm": by_v["gather"] / (kern["wf_vsa_gather"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "topk_frac_hbm": by_v["topk"] / (kern["wf_vsa_topk"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "scores_gbs": by_v["scores"] / (kern["wf_vsa_scores"] * 1e-3) / 1e9,
             "dense_equivalent_speedup": ms_dense_same / ms_vsa,
             "dense_equivalent_tflops": fl_d * wv.B / wd.B / (ms_vsa * 1e-3) / 1e12,
@@ -307,6 +359,7 @@ def main():
             "fine_tflops_page_convention": 4.0 * wv.N * 64 * k78 * wv.D * wv.Hh / (k78_ms["wf_vsa_fine"] * 1e-3) / 1e12,
             "dense_equivalent_speedup": ms_dense_same / sum(k78_ms.values()),
         },
+        "per_gpu_share": share,
         "context": {"pages_dense_ms_b200": 17.0,
                     "our_dense_ms_one_cfg_branch": ms_dense_same,
                     "pages_vsa_k78_ms_b200_persistent_cuda": 4.719},
