@@ -29,8 +29,8 @@ the numbers the pages print; see that file's header for the map.
 """
 from .dense import attention, attention_heads
 from .vsa import (CUBE, geometry, cube_layout, pool, coarse_scores, select_topk,
-                  near_tie_tolerance, fine, vsa, flops_fine, kv_stream_bytes)
+                  near_tie_tolerance, fine, vsa, coarse_output, gated, flops_fine, kv_stream_bytes)
 
 __all__ = ["attention", "attention_heads", "CUBE", "geometry", "cube_layout", "pool",
            "coarse_scores", "select_topk", "near_tie_tolerance", "fine", "vsa",
-           "flops_fine", "kv_stream_bytes"]
+           "coarse_output", "gated", "flops_fine", "kv_stream_bytes"]

@@ -29,8 +29,16 @@ Readings taken where the page is silent (each one is tested):
    selected indices are reported in ascending order.
 6. Padded key slots are masked out of the fine softmax, and padded query
    slots produce no output.
-7. The gated merge with the coarse branch needs learned gate weights and is
-   not part of this computation.
+7. The gate of the merge comes from learned weights, so it is an input here:
+   the caller supplies it (``gated``); the plain VSA output is the fine
+   stage's.
+8. The coarse branch's output for query cube c is its cube-level attention
+   over all C key cubes: the row softmax of the same scaled cube-mean scores,
+   times the key cubes' mean values (real tokens, as in reading 2).  The
+   section says the merge keeps the fine result whole and adds a learned
+   share of the coarse branch, so each real token of cube c receives
+   O = O_fine + g * O_coarse[c], elementwise, with g of the output's shape
+   [N, D] per head.  The log-sum-exp reported is the fine stage's.
 """
 from __future__ import annotations
 
@@ -150,6 +158,30 @@ def vsa(q: np.ndarray, k: np.ndarray, v: np.ndarray, T: int, H: int, W: int, top
     o, lse = fine(q, k, v, tok, plan, scale, cubes)
     return dict(qbar=qbar, kbar=kbar, scores=scores, idx=sel, margin=margin,
                 tau=near_tie_tolerance(q, k, tok, scale), o=o, lse=lse)
+
+
+def coarse_output(qbar: np.ndarray, kbar: np.ndarray, vbar: np.ndarray, scale: float) -> np.ndarray:
+    """Coarse-branch output per query cube (reading 8): softmax over all key cubes of
+    scale * Qbar_c . Kbar_c', times Vbar: [C, D]."""
+    s = coarse_scores(qbar, kbar, scale)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ vbar
+
+
+def gated(q: np.ndarray, k: np.ndarray, v: np.ndarray, tok: np.ndarray, idx: np.ndarray, scale: float,
+          gate: np.ndarray, cubes: Optional[Sequence[int]] = None):
+    """Fine output plus gate * coarse output of each token's query cube (readings 7, 8).
+
+    gate: [N, D].  Returns (o, lse) like ``fine``: rows of query cubes outside
+    ``cubes`` are NaN, and lse is the fine stage's.
+    """
+    o, lse = fine(q, k, v, tok, idx, scale, cubes)
+    oc = coarse_output(pool(q, tok), pool(k, tok), pool(v, tok), scale)
+    cube_of = np.full(q.shape[0], -1, dtype=np.int64)
+    rows, slots = np.nonzero(tok >= 0)
+    cube_of[tok[rows, slots]] = rows
+    return o + gate * oc[cube_of], lse
 
 
 def flops_fine(N: int, topk: int, D: int, heads: int, batch: int = 1) -> float:

@@ -18,6 +18,12 @@ Map of pins (function -> what fixes it):
   plan is cubes 0..k-1 and O is the mean of their real V rows; permuting
   tokens inside a key cube leaves everything unchanged; one-cube grids
   reduce to dense; a hand-made score table for the tie rule and margins.
+* oracle.coarse_output / gated: a brute force with Python loops (cube
+  membership from the coordinates, means, math.exp softmax, broadcast to
+  every real token) on a ragged grid; scipy.special.softmax on the same
+  scores; V constant gives that constant; Q = 0 gives the mean of all cube
+  means; a one-cube grid gives the mean of V; gate = 0 gives the fine output
+  exactly; the merge is linear in the gate.
 * oracle.flops_fine / kv_stream_bytes: the page's 3.35 TFLOP and 64 GB.
 """
 import json
@@ -382,3 +388,93 @@ def test_near_tie_tolerance_bounds_fp32_scores():
     s32 *= np.float32(s)
     err = np.abs(s32.astype(np.float64) - exact).max(axis=1)
     assert (err <= tau / 4).all()
+
+
+# --------------------------------------------------------------- coarse branch and gate
+
+def brute_coarse_branch(q, k, v, T, H, W, scale):
+    """Coarse-branch output broadcast to every real token, with Python loops: [N][D]."""
+    nt, nh, nw = -(-T // 4), -(-H // 4), -(-W // 4)
+    members = {}
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                members.setdefault(((t // 4) * nh + h // 4) * nw + w // 4, []).append((t * H + h) * W + w)
+    C, D = nt * nh * nw, len(q[0])
+
+    def mean(x, rows):
+        return [sum(x[r][d] for r in rows) / len(rows) for d in range(D)]
+
+    qb = [mean(q, members[c]) for c in range(C)]
+    kb = [mean(k, members[c]) for c in range(C)]
+    vb = [mean(v, members[c]) for c in range(C)]
+    out = [None] * (T * H * W)
+    for c in range(C):
+        w = [math.exp(scale * sum(qb[c][d] * kb[c2][d] for d in range(D))) for c2 in range(C)]
+        tot = sum(w)
+        oc = [sum(w[c2] * vb[c2][d] for c2 in range(C)) / tot for d in range(D)]
+        for i in members[c]:
+            out[i] = oc
+    return np.array(out)
+
+
+def small_vsa_inputs(seed, T=5, H=6, W=7, D=8):
+    N = T * H * W
+    r = rng(seed)
+    pos = np.stack(np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij"), -1).reshape(N, 3)
+    f = np.cos(pos @ r.normal(size=(3, D)) * 0.6 + r.uniform(0, 6, D))
+    return f * 2 + r.normal(size=(N, D)), f * 2 + r.normal(size=(N, D)), r.normal(size=(N, D))
+
+
+def test_coarse_branch_brute_force_ragged_grid():
+    T, H, W, D = 5, 6, 7, 8
+    q, k, v = small_vsa_inputs(31, T, H, W, D)
+    s = 1 / math.sqrt(D)
+    tok = oracle.cube_layout(T, H, W)
+    idx, _ = oracle.select_topk(oracle.coarse_scores(oracle.pool(q, tok), oracle.pool(k, tok), s), 3)
+    gate = rng(32).uniform(-1, 1, size=q.shape)
+    o, lse = oracle.gated(q, k, v, tok, idx, s, gate)
+    of, lf = oracle.fine(q, k, v, tok, idx, s)
+    ob = brute_coarse_branch(q.tolist(), k.tolist(), v.tolist(), T, H, W, s)
+    np.testing.assert_allclose(o, of + gate * ob, atol=1e-12)
+    np.testing.assert_array_equal(lse, lf)
+
+
+def test_coarse_output_matches_library_softmax():
+    from scipy.special import softmax
+    r = rng(33)
+    qb, kb, vb = r.normal(size=(11, 6)), r.normal(size=(11, 6)), r.normal(size=(11, 4))
+    p = softmax(0.4 * qb @ kb.T, axis=1)
+    np.testing.assert_allclose(oracle.coarse_output(qb, kb, vb, 0.4), p @ vb, atol=1e-13)
+
+
+def test_coarse_output_closed_forms():
+    T, H, W, D = 6, 9, 10, 16
+    q, k, v = small_vsa_inputs(34, T, H, W, D)
+    tok = oracle.cube_layout(T, H, W)
+    s = 1 / math.sqrt(D)
+    qb, kb, vb = oracle.pool(q, tok), oracle.pool(k, tok), oracle.pool(v, tok)
+    const = np.full_like(vb, 0.75)
+    np.testing.assert_allclose(oracle.coarse_output(qb, kb, const, s), 0.75, atol=1e-13)
+    oc = oracle.coarse_output(np.zeros_like(qb), kb, vb, s)  # every score ties: uniform weights
+    np.testing.assert_allclose(oc, np.broadcast_to(vb.mean(axis=0), oc.shape), atol=1e-13)
+    q1, k1, v1 = small_vsa_inputs(35, 4, 4, 4, D)  # one cube: the mean of V
+    t1 = oracle.cube_layout(4, 4, 4)
+    o1 = oracle.coarse_output(oracle.pool(q1, t1), oracle.pool(k1, t1), oracle.pool(v1, t1), s)
+    np.testing.assert_allclose(o1[0], v1.mean(axis=0), atol=1e-13)
+
+
+def test_gate_zero_and_linearity():
+    T, H, W, D = 5, 6, 7, 8
+    q, k, v = small_vsa_inputs(36, T, H, W, D)
+    tok = oracle.cube_layout(T, H, W)
+    s = 1 / math.sqrt(D)
+    idx, _ = oracle.select_topk(oracle.coarse_scores(oracle.pool(q, tok), oracle.pool(k, tok), s), 4)
+    of, _ = oracle.fine(q, k, v, tok, idx, s)
+    o0, _ = oracle.gated(q, k, v, tok, idx, s, np.zeros_like(q))
+    np.testing.assert_array_equal(o0, of)
+    g1, g2 = rng(37).normal(size=q.shape), rng(38).normal(size=q.shape)
+    d1 = oracle.gated(q, k, v, tok, idx, s, g1)[0] - of
+    d2 = oracle.gated(q, k, v, tok, idx, s, g2)[0] - of
+    d12 = oracle.gated(q, k, v, tok, idx, s, g1 + g2)[0] - of
+    np.testing.assert_allclose(d12, d1 + d2, atol=1e-12)
