@@ -101,12 +101,17 @@ def vsa_flops(wl, C) -> dict:
 
 
 def vsa_bytes(wl, C) -> dict:
-    Np = 64 * C
+    """Algorithmic HBM bytes per call of each VSA kernel (Cs: C rounded up to 32)."""
+    Np, Cs = 64 * C, (C + 31) // 32 * 32
     BH = wl.B * wl.Hh
-    gather = BH * (3 * wl.N * wl.D * 2 + 3 * Np * wl.D * 2 + 2 * C * wl.D * 4)
-    scores = BH * (2 * C * wl.D * 4 + C * C * 4)
-    topk = BH * (C * C * 4 + C * wl.topk * 4)
-    return dict(gather=gather, scores=scores, topk=topk)
+    gather = BH * (3 * wl.N * wl.D * 2 + 3 * Np * wl.D * 2 + 2 * C * wl.D * 4 + 2 * wl.D * Cs * 2)
+    scores = BH * (2 * C * wl.D * 4 + C * Cs * 4)
+    topk = BH * (C * C * 4 + C * wl.topk * 4 + C * 8)
+    # coarse-branch output: scores + row statistics + hi/lo cube means of V in, O_coarse out
+    coarse_out = BH * (C * Cs * 4 + C * 8 + 2 * wl.D * Cs * 2 + C * wl.D * 4)
+    # the gated merge adds the gate (bf16, every real token) to the fine stage's traffic
+    merge = BH * wl.N * wl.D * 2
+    return dict(gather=gather, scores=scores, topk=topk, coarse_out=coarse_out, merge=merge)
 
 
 def cpu_baseline(seconds: float) -> dict:
@@ -250,6 +255,29 @@ def main():
             k78_ms[name] = tot / n
         wf.profile_enable(False)
 
+    # extra record (not part of the step): VSA with the gated merge (coarse-branch output plus
+    # gate * O_coarse added in the fine stage's epilogue), same inputs and top-k, gate ~ U[0, 1)
+    gated_ms = None
+    if not args.no_extra:
+        gate = to_dev(synth.make_gate(wv))
+
+        def vsa_gated():
+            wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
+            wf.wf_vsa_fine_gated(ws_v, idx, gate, grid, out=ov)
+
+        vsa_gated()
+        torch.cuda.synchronize()
+        wf.profile_enable(True)
+        for _ in range(max(3, args.steps // 2)):
+            vsa_gated()
+        torch.cuda.synchronize()
+        gated_ms = {}
+        for name in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_coarse_out", "wf_vsa_fine_gated"):
+            n, tot = wf.profile_query(name)
+            gated_ms[name] = tot / n
+        wf.profile_enable(False)
+        del gate
+
     # extra record (not part of the step): one GPU's share of the heads when 8 GPUs split them
     # (5 of 40 per CFG branch): the same kernels at Hh = 5 and full N
     share = None
@@ -351,6 +379,15 @@ def main():
             "dense_equivalent_speedup": ms_dense_same / ms_vsa,
             "dense_equivalent_tflops": fl_d * wv.B / wd.B / (ms_vsa * 1e-3) / 1e12,
             "ideal_speedup": C / wv.topk,
+        },
+        "vsa_gated": None if gated_ms is None else {
+            "topk": wv.topk,
+            "ms_per_call": sum(gated_ms.values()),
+            "kernel_ms": gated_ms,
+            "coarse_out_gbs": by_v["coarse_out"] / (gated_ms["wf_vsa_coarse_out"] * 1e-3) / 1e9,
+            "coarse_out_frac_hbm": by_v["coarse_out"] / (gated_ms["wf_vsa_coarse_out"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "merge_extra_ms": gated_ms["wf_vsa_fine_gated"] - kern["wf_vsa_fine"],
+            "merge_extra_floor_ms": by_v["merge"] / PEAK_HBM_GBS / 1e6,
         },
         "vsa_k78": None if k78_ms is None else {
             "topk": k78,

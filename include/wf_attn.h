@@ -98,15 +98,18 @@ int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, flo
  * multiple of 4 ("VSA selects cubes": 21x30x52 gives 6x8x13 = 624); 0 if invalid. */
 int32_t wf_vsa_num_cubes(int32_t T, int32_t H, int32_t W);
 
-/* Workspace bytes that wf_vsa_coarse_topk fills and wf_vsa_fine reads
- * (cube-ordered Q, K and V, cube-mean Q and K, coarse scores). 0 if invalid. */
+/* Workspace bytes that wf_vsa_coarse_topk fills and the fine-stage calls read
+ * (cube-ordered Q, K and V, cube means of Q, K and V, coarse scores and their
+ * row statistics, the coarse-branch output). 0 if invalid. */
 size_t wf_vsa_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D);
 
 /*
  * VSA coarse stage ("VSA selects cubes", part 1).  With C = wf_vsa_num_cubes():
  *   1. gathers q, k, v into cube order inside `workspace` (padded slots zero);
- *   2. pools cube means Qbar, Kbar over each cube's real tokens, in fp32;
- *   3. scores S[c][c'] = scale * Qbar[c] . Kbar[c'] in fp32;
+ *   2. pools cube means Qbar, Kbar, Vbar over each cube's real tokens, in fp32
+ *      (Vbar is kept for the coarse-branch output);
+ *   3. scores S[c][c'] = scale * Qbar[c] . Kbar[c'] in fp32 and records each
+ *      row's softmax maximum and sum;
  *   4. writes idx[b][h][c][0..topk) = the topk key cubes c' with the largest
  *      S[c][c'], equal scores resolved toward the smaller c', listed in
  *      strictly ascending order.
@@ -146,6 +149,34 @@ int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v,
 int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t* idx,
                     int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
                     float scale, int32_t topk, float* o, float* lse, void* stream);
+
+/*
+ * VSA fine stage with the gated merge ("VSA selects cubes", part 3: the fine
+ * result is kept whole and a learned share of the coarse branch is added).
+ * The coarse branch's output for query cube c is the cube-level attention of
+ * the coarse stage over all C key cubes,
+ *     Oc[c] = sum_{c'} softmax_{c'}(S[c][c']) Vbar[c'],
+ * from the scores S of the preceding wf_vsa_coarse_topk (its scale), with the
+ * product P Vbar taken to about fp32 accuracy (bf16 matrix products of split
+ * hi/lo operands, fp32 sums).  Every real token i
+ * of query cube c then receives, elementwise over the head dimension,
+ *     o[i] = o_fine[i] + gate[i] * Oc[c]
+ * where o_fine is exactly what wf_vsa_fine writes (gate = 0 reproduces it bit
+ * for bit).  lse is the fine stage's.  The gate comes from learned weights
+ * in the model, so the caller supplies it.
+ *
+ *   workspace      as filled by wf_vsa_coarse_topk with the same B, Hh, T, H,
+ *                  W, D; this call also writes its coarse-output region.
+ *   gate           bf16 [B][Hh][T*H*W][D], read only.
+ *   o_coarse       fp32 [B][Hh][C][D]: Oc, written; may be NULL (it is then
+ *                  kept in the workspace only).
+ *   idx, scale, topk, o, lse, stream: as for wf_vsa_fine, including the
+ *                  WF_VALIDATE=1 plan check.
+ */
+int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t* idx,
+                          const void* gate, int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W,
+                          int32_t D, float scale, int32_t topk, float* o, float* lse,
+                          float* o_coarse, void* stream);
 
 /* ------------------------------------------------------ per-kernel timing */
 

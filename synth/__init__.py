@@ -20,6 +20,10 @@ were published separately and are not available here):
 
 Every (tensor, b, h) slice has its own PCG64 stream seeded by
 SeedSequence([seed, tensor_id, b, h]) so any slice regenerates on its own.
+
+The gate of VSA's gated merge (a learned share of the coarse branch, an
+input here) is G = bf16_RNE(u), u ~ U[0, 1) iid per element, from the stream
+of tensor id 3.
 """
 from __future__ import annotations
 
@@ -32,7 +36,7 @@ import numpy as np
 
 LENGTH_SCALE = 0.15
 FIELD_GAIN = 2.0
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "gate": 3}
 _FIELD_STREAM = 1000  # SeedSequence entropy suffix for the shared field
 
 
@@ -153,6 +157,26 @@ def make_tensor(wl: Workload, tensor: str, out: Optional[np.ndarray] = None,
     def fill(bh):
         b, h = divmod(bh, wl.Hh)
         out[b, h] = _slice(wl, tensor, b, h, phi)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(wl.B * wl.Hh)))
+    return out
+
+
+def make_gate_slice(wl: Workload, b: int, h: int) -> np.ndarray:
+    """bf16 bits [N, D] of one (b, h) slice of the gate, U[0, 1) per element."""
+    rng = np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([wl.seed, TENSOR_IDS["gate"], b, h])))
+    return bf16_bits(rng.random((wl.N, wl.D), dtype=np.float32))
+
+
+def make_gate(wl: Workload) -> np.ndarray:
+    """bf16 bits [B, Hh, N, D] of the whole gate."""
+    out = np.empty((wl.B, wl.Hh, wl.N, wl.D), dtype=np.uint16)
+
+    def fill(bh):
+        b, h = divmod(bh, wl.Hh)
+        out[b, h] = make_gate_slice(wl, b, h)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(wl.B * wl.Hh)))

@@ -25,7 +25,7 @@ def wf():
 def test_every_declared_symbol_is_exported(wf):
     names = declared_functions()
     assert "wf_attn_dense" in names and "wf_vsa_coarse_topk" in names and "wf_vsa_fine" in names
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(wf.lib, n), f"{n} declared in wf_attn.h but not exported"
 
@@ -34,7 +34,7 @@ def test_status_strings(wf):
     assert wf.lib.wf_status_string(0) == b"WF_OK"
     assert wf.lib.wf_status_string(4) == b"WF_ERR_BAD_INDEX"
     assert wf.lib.wf_status_string(99) == b"WF_UNKNOWN_STATUS"
-    assert wf.lib.wf_abi_version() == 1
+    assert wf.lib.wf_abi_version() == 2
 
 
 def test_geometry_queries(wf):
@@ -102,6 +102,14 @@ def test_vsa_argument_errors(wf):
     assert fine(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 0, FAKE, None, None) == 1
     assert fine(FAKE, 10, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None) == 3
     assert fine(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, float("inf"), 3, FAKE, None, None) == 1
+    gated = wf.lib.wf_vsa_fine_gated
+    assert gated(FAKE, 1 << 30, FAKE, None, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1
+    assert gated(FAKE, 1 << 30, FAKE, FAKE + 4, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1
+    assert gated(FAKE, 1 << 30, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, FAKE + 8, None) == 1
+    assert gated(FAKE, 1 << 30, None, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1
+    assert gated(FAKE, 1 << 30, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 9, FAKE, None, None, None) == 1
+    assert gated(FAKE, 1 << 30, FAKE, FAKE, 1, 2, 5, 6, 7, 64, 0.1, 3, FAKE, None, None, None) == 2
+    assert gated(FAKE, 10, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 3
 
 
 def test_profile_query_without_records(wf):

@@ -50,3 +50,14 @@ def test_workload_table():
     assert synth.WORKLOADS["vsa_720p"].N == 75600
     assert synth.WORKLOADS["dense_512_iid"].structured is False
     assert pytest.approx(synth.WORKLOADS["dense_512_iid"].scale) == 0.125
+
+
+def test_gate_recipe():
+    wl = synth.small_workload("g", 2, 3, 5, 6, 7, 128, seed=9)
+    g = synth.make_gate(wl)
+    assert g.shape == (2, 3, 210, 128) and g.dtype == np.uint16
+    x = synth.bits_to_f64(g)
+    assert x.min() >= 0.0 and x.max() <= 1.0
+    assert abs(x.mean() - 0.5) < 0.01
+    assert np.array_equal(synth.make_gate_slice(wl, 1, 2), g[1, 2])
+    assert not np.array_equal(g[0, 0], g[0, 1])

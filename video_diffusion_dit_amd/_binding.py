@@ -33,6 +33,8 @@ _SIGS = {
     "wf_vsa_coarse_topk": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                   _vp, _vp, _vp, _sz, _vp]),
     "wf_vsa_fine": (_i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp]),
+    "wf_vsa_fine_gated": (_i32, [_vp, _sz, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                 _vp, _vp, _vp, _vp]),
     "wf_profile_enable": (_i32, [_i32]),
     "wf_profile_query": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
                                 ctypes.POINTER(ctypes.c_double)]),
@@ -163,6 +165,35 @@ def wf_vsa_fine(workspace, idx, shape, grid, scale: Optional[float] = None, with
                            idx.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3], out.data_ptr(),
                            _ptr(lse), _stream_handle(idx.device)), "wf_vsa_fine")
     return out, lse
+
+
+def wf_vsa_fine_gated(workspace, idx, gate, grid, scale: Optional[float] = None,
+                      with_lse: bool = False, with_coarse: bool = False, out=None, lse=None,
+                      o_coarse=None):
+    """VSA fine stage plus the gated coarse branch through wf_vsa_fine_gated.
+
+    gate: bf16 [B, Hh, N, D] on the device.  Returns (o, lse or None, o_coarse
+    [B, Hh, C, D] or None).
+    """
+    torch = _torch()
+    if not gate.is_cuda or gate.dtype != torch.bfloat16 or not gate.is_contiguous() or gate.dim() != 4:
+        raise ValueError("gate must be a contiguous 4-D bfloat16 CUDA tensor [B, Hh, N, D]")
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 4:
+        raise ValueError("idx must be a contiguous int32 tensor [B, Hh, C, topk]")
+    B, Hh, N, D = gate.shape
+    T, H, W = grid
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=gate.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, N), dtype=torch.float32, device=gate.device)
+    if with_coarse and o_coarse is None:
+        o_coarse = torch.empty((B, Hh, num_cubes(T, H, W), D), dtype=torch.float32, device=gate.device)
+    _check(lib.wf_vsa_fine_gated(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 idx.data_ptr(), gate.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3],
+                                 out.data_ptr(), _ptr(lse), _ptr(o_coarse), _stream_handle(gate.device)),
+           "wf_vsa_fine_gated")
+    return out, lse, o_coarse
 
 
 def vsa(q, k, v, grid, topk: int, scale: Optional[float] = None, with_lse: bool = False,

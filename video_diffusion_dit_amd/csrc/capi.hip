@@ -124,7 +124,7 @@ const char* wf_status_string(int32_t status) {
 
 const char* wf_last_error_detail(void) { return g_detail.c_str(); }
 
-int32_t wf_abi_version(void) { return 1; }
+int32_t wf_abi_version(void) { return 2; }
 
 size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D) {
   if (!sizes_ok(B, Hh, N, D)) return 0;
@@ -206,9 +206,10 @@ int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v, int32_t 
   return ok();
 }
 
-int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t* idx, int32_t B,
-                    int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D, float scale,
-                    int32_t topk, float* o, float* lse, void* stream) {
+// Checks shared by the fine-stage entry points, then the opt-in plan check.
+static int32_t vsa_fine_checks(const void* workspace, size_t workspace_bytes, const int32_t* idx,
+                               int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                               float scale, int32_t topk, float* o, float* lse, hipStream_t s) {
   WF_CHECK_PTR(idx);
   WF_CHECK_PTR(o);
   WF_CHECK_OPT_PTR(lse);
@@ -222,7 +223,6 @@ int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t
     return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
                 L.total);
   WF_CHECK_PTR(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const char* val = getenv("WF_VALIDATE");
   if (val && val[0] == '1') {
     int bad = 0;
@@ -231,8 +231,34 @@ int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t
     if (e != hipSuccess) return hip_fail(e, "VSA plan check");
     if (bad) return fail(WF_ERR_BAD_INDEX, "top-k plan has an index outside [0, %d) or a row that is not strictly ascending", C);
   }
+  return WF_OK;
+}
+
+int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t* idx, int32_t B,
+                    int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D, float scale,
+                    int32_t topk, float* o, float* lse, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int32_t st = vsa_fine_checks(workspace, workspace_bytes, idx, B, Hh, T, H, W, D, scale, topk,
+                                   o, lse, s))
+    return st;
   hipError_t e = wf::launch_vsa_fine(workspace, idx, B * Hh, T, H, W, D, scale, topk, o, lse, s);
   if (e != hipSuccess) return hip_fail(e, "VSA fine launch");
+  return ok();
+}
+
+int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t* idx,
+                          const void* gate, int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W,
+                          int32_t D, float scale, int32_t topk, float* o, float* lse,
+                          float* o_coarse, void* stream) {
+  WF_CHECK_PTR(gate);
+  WF_CHECK_OPT_PTR(o_coarse);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int32_t st = vsa_fine_checks(workspace, workspace_bytes, idx, B, Hh, T, H, W, D, scale, topk,
+                                   o, lse, s))
+    return st;
+  hipError_t e = wf::launch_vsa_fine_gated(workspace, idx, gate, B * Hh, T, H, W, D, scale, topk, o,
+                                           lse, o_coarse, s);
+  if (e != hipSuccess) return hip_fail(e, "VSA gated fine launch");
   return ok();
 }
 

@@ -12,15 +12,20 @@
 
 namespace wf {
 
+// Cs: the cube count rounded up to a multiple of 32, the row stride of the
+// coarse scores and of the transposed cube means of V in the workspace.
 struct Grid3 {
-  int T, H, W, nt, nh, nw, C;
+  int T, H, W, nt, nh, nw, C, Cs;
 };
 
 static Grid3 make_grid(int T, int H, int W) {
-  Grid3 g{T, H, W, (T + 3) / 4, (H + 3) / 4, (W + 3) / 4, 0};
+  Grid3 g{T, H, W, (T + 3) / 4, (H + 3) / 4, (W + 3) / 4, 0, 0};
   g.C = g.nt * g.nh * g.nw;
+  g.Cs = (g.C + 31) / 32 * 32;
   return g;
 }
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // Token of slot s in cube (ct, ch, cw), or -1 for a padded slot.
 __device__ __forceinline__ int slot_token(const Grid3& g, int ct, int ch, int cw, int s) {
@@ -36,13 +41,16 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 
 // ---------------------------------------------------------------- gather + pool
 // One workgroup per (bh, cube).  Writes Qc, Kc [BH][C][64][D] (padded slots
-// zero), Vct [BH][C][D][64] (slots in perm16 order) and the fp32 means of Q and
-// K over the cube's real tokens.
+// zero), Vct [BH][C][D][64] (slots in perm16 order), the fp32 means of Q and K
+// over the cube's real tokens, and the fp32 mean of V split into two bf16
+// parts, hi = bf16(mean) and lo = bf16(mean - hi), in column c of Vbar^T
+// [2][BH][D][Cs] (hi array, then lo array; columns C..Cs-1 are zeroed, so the
+// coarse-branch product may run over whole 32-wide steps).
 template <int D>
 __global__ void __launch_bounds__(256) wf_vsa_gather(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ qc, uint16_t* __restrict__ kc, uint16_t* __restrict__ vct,
-    float* __restrict__ qbar, float* __restrict__ kbar, Grid3 g) {
+    float* __restrict__ qbar, float* __restrict__ kbar, uint16_t* __restrict__ vbt, Grid3 g) {
   constexpr int ROWCH = D / 8;            // 16-byte chunks per row
   constexpr int RSTEP = 256 / ROWCH;      // rows covered by one pass of the workgroup
   constexpr int VSTR = D + 2;
@@ -70,27 +78,34 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       if (which < 2) {
         uint16_t* dst = (which == 0 ? qc : kc) + (cube_row0 + s) * D + c16 * 8;
         *reinterpret_cast<uint4*>(dst) = u;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] += __uint_as_float((uint32_t)e[t] << 16);
       } else {
 #pragma unroll
         for (int t = 0; t < 8; ++t) vtile[s * VSTR + c16 * 8 + t] = e[t];
       }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] += __uint_as_float((uint32_t)e[t] << 16);
     }
-    if (which < 2) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) red[r0][c16 * 8 + t] = acc[t];
-      __syncthreads();
-      if (tid < D) {
-        float sum = 0.f;
+    for (int t = 0; t < 8; ++t) red[r0][c16 * 8 + t] = acc[t];
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < RSTEP; ++r) sum += red[r][tid];
-        float* dst = (which == 0 ? qbar : kbar) + ((long)bh * g.C + c) * D;
-        dst[tid] = sum / (float)count;
+      for (int r = 0; r < RSTEP; ++r) sum += red[r][tid];
+      const float mean = sum / (float)count;
+      if (which < 2) {
+        (which == 0 ? qbar : kbar)[((long)bh * g.C + c) * D + tid] = mean;
+      } else {
+        uint16_t* hi = vbt + ((long)bh * D + tid) * g.Cs;
+        uint16_t* lo = hi + (long)gridDim.x / g.C * D * g.Cs;  // gridDim.x = BH * C
+        const __bf16 h16 = (__bf16)mean;
+        hi[c] = __builtin_bit_cast(uint16_t, h16);
+        lo[c] = __builtin_bit_cast(uint16_t, (__bf16)(mean - (float)h16));
+        for (int x = g.C + c; x < g.Cs; x += g.C) hi[x] = lo[x] = 0;
       }
-      __syncthreads();
-    } else {
-      __syncthreads();
+    }
+    __syncthreads();
+    if (which == 2) {
       uint16_t* dst = vct + ((long)bh * g.C + c) * D * 64;
       for (int id = tid; id < D * 8; id += 256) {
         const int d = id / 8, pc = id % 8;
@@ -105,12 +120,13 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
 
 // ---------------------------------------------------------------- coarse scores
 // S[bh][c][c'] = scale * sum_d Qbar[c][d] Kbar[c'][d] in fp32; 64x64 output
-// tile per workgroup, 4x4 per thread.
+// tile per workgroup, 4x4 per thread.  s has row stride Cs and -inf in columns
+// C..Cs-1; s_user (optional) gets the same scores with row stride C.
 template <int D>
 __global__ void __launch_bounds__(256) wf_vsa_scores(const float* __restrict__ qbar,
                                                      const float* __restrict__ kbar,
-                                                     float* __restrict__ s, int C, int ntile,
-                                                     float scale) {
+                                                     float* __restrict__ s, float* __restrict__ s_user,
+                                                     int C, int Cs, int ntile, float scale) {
   constexpr int DK = 32;
   __shared__ float As[DK][64 + 4];
   __shared__ float Bs[DK][64 + 4];
@@ -140,7 +156,8 @@ __global__ void __launch_bounds__(256) wf_vsa_scores(const float* __restrict__ q
     }
     __syncthreads();
   }
-  float* out = s + (long)bh * C * C;
+  float* out = s + (long)bh * C * Cs;
+  float* user = s_user ? s_user + (long)bh * C * C : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = r0 + ty * 4 + i;
@@ -148,7 +165,9 @@ __global__ void __launch_bounds__(256) wf_vsa_scores(const float* __restrict__ q
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int cc = c0 + tx * 4 + jj;
-      if (cc < C) out[(long)r * C + cc] = acc[i][jj] * scale;
+      const float x = acc[i][jj] * scale;
+      if (cc < Cs) out[(long)r * Cs + cc] = cc < C ? x : -INFINITY;
+      if (user && cc < C) user[(long)r * C + cc] = x;
     }
   }
 }
@@ -157,21 +176,36 @@ __global__ void __launch_bounds__(256) wf_vsa_scores(const float* __restrict__ q
 // One wavefront per score row.  Lane L holds candidates c' = e*64 + L.  The
 // k-th largest order key is found bit by bit (count of keys >= candidate via
 // ballots); keys above it are all kept, keys equal to it are kept in
-// ascending c' order until k are chosen.  Output is ascending.
+// ascending c' order until k are chosen.  Output is ascending.  The wavefront
+// also records the row's softmax statistics for the coarse-branch output:
+// stat[row] = (log2(e) * max_c' S, 1 / sum_c' 2^(log2(e) S - that)).
 template <int E>
 __global__ void __launch_bounds__(256) wf_vsa_topk(const float* __restrict__ s,
-                                                   int* __restrict__ idx, long rows, int C,
-                                                   int k) {
+                                                   int* __restrict__ idx, float2* __restrict__ stat,
+                                                   long rows, int C, int Cs, int k) {
   const int lane = threadIdx.x % 64;
   const long row = (long)blockIdx.x * 4 + threadIdx.x / 64;
   if (row >= rows) return;
-  const float* sr = s + row * C;
+  const float* sr = s + row * Cs;
   uint32_t key[E];
+  float val[E];
+  float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int cc = e * 64 + lane;
-    key[e] = cc < C ? order_key(sr[cc]) : 0u;
+    val[e] = cc < C ? sr[cc] : -INFINITY;
+    key[e] = cc < C ? order_key(val[e]) : 0u;
+    mx = fmaxf(mx, val[e]);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float ml = mx * kLog2e;
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(val[e], kLog2e, -ml));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (lane == 0) stat[row] = make_float2(ml, 1.f / sum);
   uint32_t thr = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = thr | (1u << b);
@@ -200,6 +234,109 @@ __global__ void __launch_bounds__(256) wf_vsa_topk(const float* __restrict__ s,
   }
 }
 
+// ---------------------------------------------------------------- coarse-branch output
+// Oc[bh][c] = sum_c' softmax_c'(S[c][c']) Vbar[c'], the cube-level attention
+// of the coarse stage, from the fp32 scores and the row statistics the top-k
+// kernel recorded (so P is final: no running max, no rescale).  One workgroup
+// per (bh, 64 query cubes); wavefront w takes query cubes 32*(w&1) .. +32 and
+// head dims 64*(w>>1) .. +64:
+//   Oc^T (64 x 32) = Vbar^T (64 x Cs) . P^T (Cs x 32), MFMA 32x32x16 bf16,
+// with both operands split into bf16 hi and lo parts and the three products
+// hi.hi + lo.hi + hi.lo summed in fp32: an error near fp32's, where bf16
+// operands alone would carry Vbar's rounding straight into Oc (the softmax
+// over cubes is usually dominated by one cube).  Each lane builds its B
+// operand straight from one score row (one query cube, 8 consecutive key
+// cubes) and reads its A operand (8 consecutive key cubes of one head dim)
+// from Vbar^T; both operands index key cubes the same way, so the product
+// pairs them correctly.  Padded key columns hold -inf scores and zero means,
+// so they add nothing.
+template <int D>
+__global__ void __launch_bounds__(256) wf_vsa_coarse_out(const float* __restrict__ s,
+                                                         const float2* __restrict__ stat,
+                                                         const uint16_t* __restrict__ vbt,
+                                                         float* __restrict__ oc, int C, int Cs,
+                                                         int rblocks) {
+  static_assert(D == 128, "two 32-wide head-dim blocks per wavefront, two wavefront columns");
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64,
+            j = lane % 32, half = lane / 32;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = item / rblocks, rb = item % rblocks;
+  const int r = rb * 64 + (wave & 1) * 32 + j, rr = min(r, C - 1);
+  const int d0 = (wave >> 1) * 64;
+  const float2 st = stat[(long)bh * C + rr];
+  const float* srow = s + ((long)bh * C + rr) * Cs + half * 8;
+  const uint16_t* va = vbt + ((long)bh * D + d0 + j) * Cs + half * 8;  // hi part
+  const long lo_off = (long)gridDim.x / rblocks * D * Cs;  // lo array follows hi (gridDim.x = BH * rblocks)
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
+  for (int k0 = 0; k0 < Cs; k0 += 32) {  // Cs is a multiple of 32: two k-steps of 16 key cubes
+    float4 x[4];
+    uint4 a[8];  // per k-step: block 0 hi, block 1 hi, block 0 lo, block 1 lo
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      x[2 * h] = *reinterpret_cast<const float4*>(srow + k0 + 16 * h);
+      x[2 * h + 1] = *reinterpret_cast<const float4*>(srow + k0 + 16 * h + 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        a[4 * h + u] = *reinterpret_cast<const uint4*>(va + (u >> 1) * lo_off + (u & 1) * 32 * Cs + k0 + 16 * h);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float xs[8] = {x[2 * h].x, x[2 * h].y, x[2 * h].z, x[2 * h].w,
+                           x[2 * h + 1].x, x[2 * h + 1].y, x[2 * h + 1].z, x[2 * h + 1].w};
+      f32x8 pf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[i], kLog2e, -st.x)) * st.y;
+      const bf16x8 ph = __builtin_convertvector(pf, bf16x8);
+      const bf16x8 pl = __builtin_convertvector(pf - __builtin_convertvector(ph, f32x8), bf16x8);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 2]), ph, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 3]), ph, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h]), pl, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 1]), pl, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h]), ph, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 1]), ph, acc1, 0, 0, 0);
+    }
+  }
+  if (r >= C) return;
+  float* orow = oc + ((long)bh * C + r) * D + d0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    *reinterpret_cast<float4*>(orow + q * 8 + half * 4) =
+        make_float4(acc0[q * 4], acc0[q * 4 + 1], acc0[q * 4 + 2], acc0[q * 4 + 3]);
+    *reinterpret_cast<float4*>(orow + 32 + q * 8 + half * 4) =
+        make_float4(acc1[q * 4], acc1[q * 4 + 1], acc1[q * 4 + 2], acc1[q * 4 + 3]);
+  }
+}
+
+// Fine-stage epilogue with the gated merge: the normalised fine output plus
+// gate * Oc of the token's query cube, elementwise.  Lane (j, half) holds head
+// dims b*32 + rq*8 + half*4 + 0..3 of its query row (the MFMA output layout).
+template <int DB>
+__device__ __forceinline__ float finish_store_gated(const f32x16* o, float m, float l,
+                                                    float* __restrict__ orow,
+                                                    const uint16_t* __restrict__ grow,
+                                                    const float* __restrict__ ocrow, int half) {
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.f / lt;
+  if (orow) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = b * 32 + rq * 8 + half * 4;
+        const float4 c4 = *reinterpret_cast<const float4*>(ocrow + d);
+        const uint2 g2 = *reinterpret_cast<const uint2*>(grow + d);
+        const float g0 = __uint_as_float(g2.x << 16), g1 = __uint_as_float(g2.x & 0xFFFF0000u),
+                    g3 = __uint_as_float(g2.y & 0xFFFF0000u), gg2 = __uint_as_float(g2.y << 16);
+        *reinterpret_cast<float4*>(orow + d) = make_float4(
+            __builtin_fmaf(g0, c4.x, o[b][rq * 4] * inv), __builtin_fmaf(g1, c4.y, o[b][rq * 4 + 1] * inv),
+            __builtin_fmaf(gg2, c4.z, o[b][rq * 4 + 2] * inv), __builtin_fmaf(g3, c4.w, o[b][rq * 4 + 3] * inv));
+      }
+  }
+  return (m + __builtin_amdgcn_logf(lt)) * kLn2;
+}
+
 // ---------------------------------------------------------------- fine stage
 // One workgroup (2 wavefronts x 32 query slots) per (bh, query cube); it walks
 // the k selected key cubes, one cube (64 keys) per tile.  K and V^T of the
@@ -210,12 +347,14 @@ __global__ void __launch_bounds__(256) wf_vsa_topk(const float* __restrict__ s,
 // copy of the next V cube starts once both have accumulated P V and is waited
 // for only before the next P V, so it lands behind the next tile's scores and
 // softmax.  Padded key slots of edge cubes are masked; output rows are
-// scattered back to grid order, padded query slots are not written.
-template <int D>
+// scattered back to grid order, padded query slots are not written.  With
+// GATED the epilogue adds gate * Oc of the query cube (gated merge).
+template <int D, bool GATED>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vct, const int* __restrict__ idx, float* __restrict__ o,
-    float* __restrict__ lse, Grid3 g, int k, float sl2) {
+    float* __restrict__ lse, const uint16_t* __restrict__ gate, const float* __restrict__ ocoarse,
+    Grid3 g, int k, float sl2) {
   constexpr int DB = D / 32, NPV = Pairs<D>::NPV, NQK = Pairs<D>::NQK;
   __shared__ __align__(16) char ks[Swz<D>::KB];
   __shared__ __align__(16) char vs[Swz<D>::VB];
@@ -280,7 +419,12 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   cube_coords(g, c, ct, ch, cw);
   const int tok = slot_token(g, ct, ch, cw, slot);
   const long row = (long)bh * g.T * g.H * g.W + tok;
-  const float lse_row = finish_store<DB>(oacc, m, l, tok >= 0 ? o + row * D : nullptr, half);
+  float lse_row;
+  if constexpr (GATED)
+    lse_row = finish_store_gated<DB>(oacc, m, l, tok >= 0 ? o + row * D : nullptr, gate + row * D,
+                                     ocoarse + (cube_base + c) * D, half);
+  else
+    lse_row = finish_store<DB>(oacc, m, l, tok >= 0 ? o + row * D : nullptr, half);
   if (lse && tok >= 0 && half == 0) lse[row] = lse_row;
 }
 
@@ -314,8 +458,11 @@ VsaLayout vsa_layout(int BH, int T, int H, int W, int D) {
   L.vct = L.kc + up(tok);
   L.qbar = L.vct + up(tok);
   L.kbar = L.qbar + up((size_t)BH * g.C * D * 4);
-  L.scores = L.kbar + up((size_t)BH * g.C * D * 4);
-  L.flag = L.scores + up((size_t)BH * g.C * g.C * 4);
+  L.vbt = L.kbar + up((size_t)BH * g.C * D * 4);
+  L.scores = L.vbt + up((size_t)2 * BH * D * g.Cs * 2);
+  L.stat = L.scores + up((size_t)BH * g.C * g.Cs * 4);
+  L.ocoarse = L.stat + up((size_t)BH * g.C * 8);
+  L.flag = L.ocoarse + up((size_t)BH * g.C * D * 4);
   L.total = L.flag + 256;
   return L;
 }
@@ -329,28 +476,30 @@ hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH
   auto qc = reinterpret_cast<uint16_t*>(w + L.qc), kc = reinterpret_cast<uint16_t*>(w + L.kc),
        vct = reinterpret_cast<uint16_t*>(w + L.vct);
   auto qbar = reinterpret_cast<float*>(w + L.qbar), kbar = reinterpret_cast<float*>(w + L.kbar);
-  float* sc = scores_out ? scores_out : reinterpret_cast<float*>(w + L.scores);
+  auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
+  auto sc = reinterpret_cast<float*>(w + L.scores);
+  auto stat = reinterpret_cast<float2*>(w + L.stat);
   hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
     hipLaunchKernelGGL(wf_vsa_gather<128>, dim3((unsigned)(BH * g.C)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), qc, kc, vct, qbar, kbar, g);
+                       static_cast<const uint16_t*>(v), qc, kc, vct, qbar, kbar, vbt, g);
   });
   if (e != hipSuccess) return e;
   const int nt = (g.C + 63) / 64;
   e = wf_launch("wf_vsa_scores", s, [&] {
     hipLaunchKernelGGL(wf_vsa_scores<128>, dim3((unsigned)(BH * nt * nt)), dim3(256), 0, s, qbar,
-                       kbar, sc, g.C, nt, scale);
+                       kbar, sc, scores_out, g.C, g.Cs, nt, scale);
   });
   if (e != hipSuccess) return e;
   const long rows = (long)BH * g.C;
   const dim3 grid((unsigned)((rows + 3) / 4));
   return wf_launch("wf_vsa_topk", s, [&] {
     if (g.C <= 1024)
-      hipLaunchKernelGGL(wf_vsa_topk<16>, grid, dim3(256), 0, s, sc, idx, rows, g.C, topk);
+      hipLaunchKernelGGL(wf_vsa_topk<16>, grid, dim3(256), 0, s, sc, idx, stat, rows, g.C, g.Cs, topk);
     else if (g.C <= 2048)
-      hipLaunchKernelGGL(wf_vsa_topk<32>, grid, dim3(256), 0, s, sc, idx, rows, g.C, topk);
+      hipLaunchKernelGGL(wf_vsa_topk<32>, grid, dim3(256), 0, s, sc, idx, stat, rows, g.C, g.Cs, topk);
     else
-      hipLaunchKernelGGL(wf_vsa_topk<64>, grid, dim3(256), 0, s, sc, idx, rows, g.C, topk);
+      hipLaunchKernelGGL(wf_vsa_topk<64>, grid, dim3(256), 0, s, sc, idx, stat, rows, g.C, g.Cs, topk);
   });
 }
 
@@ -377,10 +526,35 @@ hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H,
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   const char* w = static_cast<const char*>(ws);
   return wf_launch("wf_vsa_fine", s, [&] {
-    hipLaunchKernelGGL(wf_vsa_fine_fwd<128>, dim3((unsigned)(BH * g.C)), dim3(128), 0, s, reinterpret_cast<const uint16_t*>(w + L.qc),
+    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, false>), dim3((unsigned)(BH * g.C)), dim3(128), 0, s,
+                       reinterpret_cast<const uint16_t*>(w + L.qc),
                        reinterpret_cast<const uint16_t*>(w + L.kc),
-                       reinterpret_cast<const uint16_t*>(w + L.vct), idx, o, lse, g, topk,
-                       scale * kLog2e);
+                       reinterpret_cast<const uint16_t*>(w + L.vct), idx, o, lse, nullptr, nullptr,
+                       g, topk, scale * kLog2e);
+  });
+}
+
+hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int BH, int T, int H,
+                                 int W, int D, float scale, int topk, float* o, float* lse,
+                                 float* o_coarse, hipStream_t s) {
+  const Grid3 g = make_grid(T, H, W);
+  const VsaLayout L = vsa_layout(BH, T, H, W, D);
+  char* w = static_cast<char*>(ws);
+  float* oc = o_coarse ? o_coarse : reinterpret_cast<float*>(w + L.ocoarse);
+  const int rblocks = (g.C + 63) / 64;
+  hipError_t e = wf_launch("wf_vsa_coarse_out", s, [&] {
+    hipLaunchKernelGGL(wf_vsa_coarse_out<128>, dim3((unsigned)(BH * rblocks)), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(w + L.scores),
+                       reinterpret_cast<const float2*>(w + L.stat),
+                       reinterpret_cast<const uint16_t*>(w + L.vbt), oc, g.C, g.Cs, rblocks);
+  });
+  if (e != hipSuccess) return e;
+  return wf_launch("wf_vsa_fine_gated", s, [&] {
+    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, true>), dim3((unsigned)(BH * g.C)), dim3(128), 0, s,
+                       reinterpret_cast<const uint16_t*>(w + L.qc),
+                       reinterpret_cast<const uint16_t*>(w + L.kc),
+                       reinterpret_cast<const uint16_t*>(w + L.vct), idx, o, lse,
+                       static_cast<const uint16_t*>(gate), oc, g, topk, scale * kLog2e);
   });
 }
 

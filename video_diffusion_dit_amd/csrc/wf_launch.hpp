@@ -28,7 +28,7 @@ hipError_t launch_dense(const void* q, const void* k, const void* v, float* o, f
 // VSA workspace layout (byte offsets, each 256-byte aligned).
 struct VsaLayout {
   int C;
-  size_t qc, kc, vct, qbar, kbar, scores, flag, total;
+  size_t qc, kc, vct, qbar, kbar, vbt, scores, stat, ocoarse, flag, total;
 };
 VsaLayout vsa_layout(int BH, int T, int H, int W, int D);
 hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH, int T, int H,
@@ -38,5 +38,8 @@ hipError_t launch_vsa_check(const int* idx, int BH, int C, int topk, void* ws, s
                             hipStream_t s, int* bad);
 hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H, int W, int D,
                            float scale, int topk, float* o, float* lse, hipStream_t s);
+hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int BH, int T, int H,
+                                 int W, int D, float scale, int topk, float* o, float* lse,
+                                 float* o_coarse, hipStream_t s);
 
 }  // namespace wf
