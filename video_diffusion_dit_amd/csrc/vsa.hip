@@ -27,6 +27,15 @@ static Grid3 make_grid(int T, int H, int W) {
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
+// Element offset of (part, head, key cube, head dim) in the cube means of V,
+// stored in the lane order of the coarse-branch MFMA's A operand so that one
+// load of a wavefront reads 1 KiB contiguously: [part hi/lo][bh][key step of
+// 16][dim block of 32][lane 0..63][8 key cubes], lane = dim % 32 + 32 * (key % 16 / 8).
+__device__ __forceinline__ long vbar_index(int part, int bh, int BH, int Cs, int key, int d) {
+  const int lane = d % 32 + 32 * ((key % 16) / 8);
+  return ((((long)part * BH + bh) * (Cs / 16) + key / 16) * 4 + d / 32) * 512 + lane * 8 + key % 8;
+}
+
 // Token of slot s in cube (ct, ch, cw), or -1 for a padded slot.
 __device__ __forceinline__ int slot_token(const Grid3& g, int ct, int ch, int cw, int s) {
   const int t = ct * 4 + (s >> 4), h = ch * 4 + ((s >> 2) & 3), w = cw * 4 + (s & 3);
@@ -43,8 +52,8 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 // One workgroup per (bh, cube).  Writes Qc, Kc [BH][C][64][D] (padded slots
 // zero), Vct [BH][C][D][64] (slots in perm16 order), the fp32 means of Q and K
 // over the cube's real tokens, and the fp32 mean of V split into two bf16
-// parts, hi = bf16(mean) and lo = bf16(mean - hi), in column c of Vbar^T
-// [2][BH][D][Cs] (hi array, then lo array; columns C..Cs-1 are zeroed, so the
+// parts, hi = bf16(mean) and lo = bf16(mean - hi), at key cube c of the
+// operand-ordered means (vbar_index; key cubes C..Cs-1 are zeroed, so the
 // coarse-branch product may run over whole 32-wide steps).
 template <int D>
 __global__ void __launch_bounds__(256) wf_vsa_gather(
@@ -96,12 +105,13 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       if (which < 2) {
         (which == 0 ? qbar : kbar)[((long)bh * g.C + c) * D + tid] = mean;
       } else {
-        uint16_t* hi = vbt + ((long)bh * D + tid) * g.Cs;
-        uint16_t* lo = hi + (long)gridDim.x / g.C * D * g.Cs;  // gridDim.x = BH * C
+        static_assert(D == 128, "four 32-wide head-dim blocks");
+        const int BH = gridDim.x / g.C;  // gridDim.x = BH * C
         const __bf16 h16 = (__bf16)mean;
-        hi[c] = __builtin_bit_cast(uint16_t, h16);
-        lo[c] = __builtin_bit_cast(uint16_t, (__bf16)(mean - (float)h16));
-        for (int x = g.C + c; x < g.Cs; x += g.C) hi[x] = lo[x] = 0;
+        vbt[vbar_index(0, bh, BH, g.Cs, c, tid)] = __builtin_bit_cast(uint16_t, h16);
+        vbt[vbar_index(1, bh, BH, g.Cs, c, tid)] = __builtin_bit_cast(uint16_t, (__bf16)(mean - (float)h16));
+        for (int x = g.C + c; x < g.Cs; x += g.C)
+          vbt[vbar_index(0, bh, BH, g.Cs, x, tid)] = vbt[vbar_index(1, bh, BH, g.Cs, x, tid)] = 0;
       }
     }
     __syncthreads();
@@ -238,74 +248,98 @@ __global__ void __launch_bounds__(256) wf_vsa_topk(const float* __restrict__ s,
 // Oc[bh][c] = sum_c' softmax_c'(S[c][c']) Vbar[c'], the cube-level attention
 // of the coarse stage, from the fp32 scores and the row statistics the top-k
 // kernel recorded (so P is final: no running max, no rescale).  One workgroup
-// per (bh, 64 query cubes); wavefront w takes query cubes 32*(w&1) .. +32 and
-// head dims 64*(w>>1) .. +64:
-//   Oc^T (64 x 32) = Vbar^T (64 x Cs) . P^T (Cs x 32), MFMA 32x32x16 bf16,
+// per (bh, 32 query cubes); its four wavefronts take interleaved steps of 16
+// key cubes (wavefront w: steps w, w+4, ...), each accumulating all D head
+// dims, and the four partial sums are added through LDS at the end:
+//   Oc^T (D x 32) = Vbar^T (D x Cs) . P^T (Cs x 32), MFMA 32x32x16 bf16,
 // with both operands split into bf16 hi and lo parts and the three products
 // hi.hi + lo.hi + hi.lo summed in fp32: an error near fp32's, where bf16
 // operands alone would carry Vbar's rounding straight into Oc (the softmax
 // over cubes is usually dominated by one cube).  Each lane builds its B
 // operand straight from one score row (one query cube, 8 consecutive key
-// cubes) and reads its A operand (8 consecutive key cubes of one head dim)
-// from Vbar^T; both operands index key cubes the same way, so the product
-// pairs them correctly.  Padded key columns hold -inf scores and zero means,
-// so they add nothing.
+// cubes) and reads its A operands (8 consecutive key cubes of one head dim)
+// from the operand-ordered means, 1 KiB per wavefront and load; both operands
+// index key cubes the same way, so the product pairs them correctly.  The next step's operands are loaded before the
+// current step's products.  Padded key columns hold -inf scores and zero
+// means, so they add nothing.
+template <int D>
+struct CoarseStep {
+  float4 x[2];          // 8 scores of this lane's query cube
+  uint4 a[2 * (D / 32)];  // Vbar^T hi (blocks 0..DB-1), then lo
+};
+
+template <int D>
+__device__ __forceinline__ void coarse_load(CoarseStep<D>& st, const float* srow, const uint16_t* va,
+                                            long lo_off, int t) {
+  constexpr int DB = D / 32;
+  st.x[0] = *reinterpret_cast<const float4*>(srow + t * 16);
+  st.x[1] = *reinterpret_cast<const float4*>(srow + t * 16 + 4);
+#pragma unroll
+  for (int u = 0; u < 2 * DB; ++u)
+    st.a[u] = *reinterpret_cast<const uint4*>(va + (u / DB) * lo_off + ((long)t * DB + u % DB) * 512);
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) wf_vsa_coarse_out(const float* __restrict__ s,
                                                          const float2* __restrict__ stat,
                                                          const uint16_t* __restrict__ vbt,
                                                          float* __restrict__ oc, int C, int Cs,
                                                          int rblocks) {
-  static_assert(D == 128, "two 32-wide head-dim blocks per wavefront, two wavefront columns");
+  constexpr int DB = D / 32;
+  __shared__ float part[4][DB][16][64];  // per wavefront: DB accumulator blocks, register-major
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64,
             j = lane % 32, half = lane / 32;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / rblocks, rb = item % rblocks;
-  const int r = rb * 64 + (wave & 1) * 32 + j, rr = min(r, C - 1);
-  const int d0 = (wave >> 1) * 64;
+  const int r = rb * 32 + j, rr = min(r, C - 1);
   const float2 st = stat[(long)bh * C + rr];
   const float* srow = s + ((long)bh * C + rr) * Cs + half * 8;
-  const uint16_t* va = vbt + ((long)bh * D + d0 + j) * Cs + half * 8;  // hi part
-  const long lo_off = (long)gridDim.x / rblocks * D * Cs;  // lo array follows hi (gridDim.x = BH * rblocks)
-  f32x16 acc0, acc1;
+  const int BH = gridDim.x / rblocks;  // gridDim.x = BH * rblocks
+  const uint16_t* va = vbt + vbar_index(0, bh, BH, Cs, 0, 0) + lane * 8;  // hi part, step 0, block 0
+  const long lo_off = (long)BH * D * Cs;                                    // lo part follows hi
+  f32x16 acc[DB];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
-  for (int k0 = 0; k0 < Cs; k0 += 32) {  // Cs is a multiple of 32: two k-steps of 16 key cubes
-    float4 x[4];
-    uint4 a[8];  // per k-step: block 0 hi, block 1 hi, block 0 lo, block 1 lo
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      x[2 * h] = *reinterpret_cast<const float4*>(srow + k0 + 16 * h);
-      x[2 * h + 1] = *reinterpret_cast<const float4*>(srow + k0 + 16 * h + 4);
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+  const int nsteps = Cs / 16;
+  CoarseStep<D> cur, nxt;
+  if (wave < nsteps) coarse_load<D>(cur, srow, va, lo_off, wave);
+  for (int t = wave; t < nsteps; t += 4) {
+    const int tn = t + 4 < nsteps ? t + 4 : t;  // past the end: reload the current step (in bounds)
+    coarse_load<D>(nxt, srow, va, lo_off, tn);
+    const float xs[8] = {cur.x[0].x, cur.x[0].y, cur.x[0].z, cur.x[0].w,
+                         cur.x[1].x, cur.x[1].y, cur.x[1].z, cur.x[1].w};
+    f32x8 pf;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        a[4 * h + u] = *reinterpret_cast<const uint4*>(va + (u >> 1) * lo_off + (u & 1) * 32 * Cs + k0 + 16 * h);
+    for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[i], kLog2e, -st.x)) * st.y;
+    const bf16x8 ph = __builtin_convertvector(pf, bf16x8);
+    const bf16x8 pl = __builtin_convertvector(pf - __builtin_convertvector(ph, f32x8), bf16x8);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.a[DB + b]), ph, acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.a[b]), pl, acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.a[b]), ph, acc[b], 0, 0, 0);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float xs[8] = {x[2 * h].x, x[2 * h].y, x[2 * h].z, x[2 * h].w,
-                           x[2 * h + 1].x, x[2 * h + 1].y, x[2 * h + 1].z, x[2 * h + 1].w};
-      f32x8 pf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[i], kLog2e, -st.x)) * st.y;
-      const bf16x8 ph = __builtin_convertvector(pf, bf16x8);
-      const bf16x8 pl = __builtin_convertvector(pf - __builtin_convertvector(ph, f32x8), bf16x8);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 2]), ph, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 3]), ph, acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h]), pl, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 1]), pl, acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h]), ph, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[4 * h + 1]), ph, acc1, 0, 0, 0);
-    }
+    cur = nxt;
   }
-  if (r >= C) return;
-  float* orow = oc + ((long)bh * C + r) * D + d0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    *reinterpret_cast<float4*>(orow + q * 8 + half * 4) =
-        make_float4(acc0[q * 4], acc0[q * 4 + 1], acc0[q * 4 + 2], acc0[q * 4 + 3]);
-    *reinterpret_cast<float4*>(orow + 32 + q * 8 + half * 4) =
-        make_float4(acc1[q * 4], acc1[q * 4 + 1], acc1[q * 4 + 2], acc1[q * 4 + 3]);
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[wave][b][i][lane] = acc[b][i];
+  __syncthreads();
+  // wavefront w adds up accumulator block w (D = 128: one block each) and stores it
+  for (int b = wave; b < DB; b += 4) {
+    float o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      o[i] = (part[0][b][i][lane] + part[1][b][i][lane]) + (part[2][b][i][lane] + part[3][b][i][lane]);
+    if (r < C) {
+      float* orow = oc + ((long)bh * C + r) * D + b * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(orow + q * 8 + half * 4) = make_float4(o[q * 4], o[q * 4 + 1], o[q * 4 + 2], o[q * 4 + 3]);
+    }
   }
 }
 
@@ -541,7 +575,7 @@ hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   char* w = static_cast<char*>(ws);
   float* oc = o_coarse ? o_coarse : reinterpret_cast<float*>(w + L.ocoarse);
-  const int rblocks = (g.C + 63) / 64;
+  const int rblocks = (g.C + 31) / 32;
   hipError_t e = wf_launch("wf_vsa_coarse_out", s, [&] {
     hipLaunchKernelGGL(wf_vsa_coarse_out<128>, dim3((unsigned)(BH * rblocks)), dim3(256), 0, s,
                        reinterpret_cast<const float*>(w + L.scores),
