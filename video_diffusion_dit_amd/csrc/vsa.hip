@@ -343,32 +343,50 @@ __global__ void __launch_bounds__(256) wf_vsa_coarse_out(const float* __restrict
   }
 }
 
-// Fine-stage epilogue with the gated merge: the normalised fine output plus
-// gate * Oc of the token's query cube, elementwise.  Lane (j, half) holds head
-// dims b*32 + rq*8 + half*4 + 0..3 of its query row (the MFMA output layout).
-template <int DB>
-__device__ __forceinline__ float finish_store_gated(const f32x16* o, float m, float l,
-                                                    float* __restrict__ orow,
-                                                    const uint16_t* __restrict__ grow,
-                                                    const float* __restrict__ ocrow, int half) {
-  const float lt = l + __shfl_xor(l, 32);
-  const float inv = 1.f / lt;
-  if (orow) {
+// Fine-stage epilogue: the normalised output rows of a wavefront go through
+// its own LDS slot (32 rows x D fp32 = 16 KiB, the K or V slot, free once the
+// sweep is done), so that global stores cover two whole token rows per
+// instruction instead of 16 bytes of 32 different rows.  In LDS, row r's
+// 16-byte chunk c sits at chunk c ^ (r % 32), which keeps both the scattered
+// writes and the row reads free of bank conflicts.  With GATED the merge
+// O = O_fine + gate * Oc is applied on the way out, where the gate is read
+// row-contiguously as well.
+template <int D, bool GATED>
+__device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* slot_lds, int j, int half,
+                                              const Grid3& g, int ct, int ch, int cw, int wave, long head_row0,
+                                              float* __restrict__ out, const uint16_t* __restrict__ gate,
+                                              const float* __restrict__ ocube) {
+  constexpr int DB = D / 32, CH = D / 4;  // 16-byte chunks per row
+  static_assert(CH == 32, "row swizzle assumes 32 chunks per row");
+  float* lds = reinterpret_cast<float*>(slot_lds);
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d = b * 32 + rq * 8 + half * 4;
-        const float4 c4 = *reinterpret_cast<const float4*>(ocrow + d);
-        const uint2 g2 = *reinterpret_cast<const uint2*>(grow + d);
-        const float g0 = __uint_as_float(g2.x << 16), g1 = __uint_as_float(g2.x & 0xFFFF0000u),
-                    g3 = __uint_as_float(g2.y & 0xFFFF0000u), gg2 = __uint_as_float(g2.y << 16);
-        *reinterpret_cast<float4*>(orow + d) = make_float4(
-            __builtin_fmaf(g0, c4.x, o[b][rq * 4] * inv), __builtin_fmaf(g1, c4.y, o[b][rq * 4 + 1] * inv),
-            __builtin_fmaf(gg2, c4.z, o[b][rq * 4 + 2] * inv), __builtin_fmaf(g3, c4.w, o[b][rq * 4 + 3] * inv));
+    for (int rq = 0; rq < 4; ++rq) {
+      const int c = (b * 32 + rq * 8 + half * 4) / 4;
+      *reinterpret_cast<float4*>(lds + j * D + ((c ^ j) * 4)) =
+          make_float4(o[b][rq * 4] * inv, o[b][rq * 4 + 1] * inv, o[b][rq * 4 + 2] * inv, o[b][rq * 4 + 3] * inv);
+    }
+  asm volatile("" ::: "memory");  // this wavefront's LDS writes precede its reads (LDS keeps wave order)
+  const int lane = half * 32 + j, c = lane % 32;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = 2 * i + lane / 32;  // row inside this wavefront's 32
+    const int tok = slot_token(g, ct, ch, cw, wave * 32 + r);
+    float4 v = *reinterpret_cast<const float4*>(lds + r * D + ((c ^ r) * 4));
+    if (tok >= 0) {
+      const long row = head_row0 + tok;
+      if constexpr (GATED) {
+        const float4 c4 = *reinterpret_cast<const float4*>(ocube + c * 4);
+        const uint2 g2 = *reinterpret_cast<const uint2*>(gate + row * D + c * 4);
+        v.x = __builtin_fmaf(__uint_as_float(g2.x << 16), c4.x, v.x);
+        v.y = __builtin_fmaf(__uint_as_float(g2.x & 0xFFFF0000u), c4.y, v.y);
+        v.z = __builtin_fmaf(__uint_as_float(g2.y << 16), c4.z, v.z);
+        v.w = __builtin_fmaf(__uint_as_float(g2.y & 0xFFFF0000u), c4.w, v.w);
       }
+      *reinterpret_cast<float4*>(out + row * D + c * 4) = v;
+    }
   }
-  return (m + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------- fine stage
@@ -448,18 +466,16 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     wait_tile_copies_keep<VP>();  // K(t+1) landed; V(t+1) may fly
     cur = nxt;
   }
-  wait_tile_copies();  // no copy may still be writing LDS when the workgroup ends
+  wait_tile_copies();  // this wavefront's copies (the last ones are redundant) have landed
+  barrier_nofence();   // every wavefront is done with both slots
   int ct, ch, cw;
   cube_coords(g, c, ct, ch, cw);
+  const long head_row0 = (long)bh * g.T * g.H * g.W;
+  const float lt = l + __shfl_xor(l, 32);
+  fine_epilogue<D, GATED>(oacc, 1.f / lt, wave == 0 ? ks : vs, j, half, g, ct, ch, cw, wave, head_row0, o,
+                          gate, GATED ? ocoarse + (cube_base + c) * D : nullptr);
   const int tok = slot_token(g, ct, ch, cw, slot);
-  const long row = (long)bh * g.T * g.H * g.W + tok;
-  float lse_row;
-  if constexpr (GATED)
-    lse_row = finish_store_gated<DB>(oacc, m, l, tok >= 0 ? o + row * D : nullptr, gate + row * D,
-                                     ocoarse + (cube_base + c) * D, half);
-  else
-    lse_row = finish_store<DB>(oacc, m, l, tok >= 0 ? o + row * D : nullptr, half);
-  if (lse && tok >= 0 && half == 0) lse[row] = lse_row;
+  if (lse && tok >= 0 && half == 0) lse[head_row0 + tok] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------- plan check
