@@ -18,6 +18,10 @@ Sources (cited by page title and section; no code is printed on the pages):
   is exact and stable; a fixed constant can overflow).
 * "Wan2.1 acceleration" blog (bafh001.com), section 4.2: attention is
   called non-causally, with QK^T, softmax and PV fused block-wise on chip.
+* "推理优化" (Inference optimization, WorldFoundry docs), section "Exact or
+  numerically equivalent Wan kernels", entry fused_rope: a fused 3D RoPE
+  with an fp32 or fp64 rotation (oracle/rope.py states the definition
+  adopted, since the page gives no frequencies).
 
 Readings taken where the pages are silent are listed in each function's
 docstring.  All functions take float64 numpy arrays (bf16 inputs widened
@@ -28,9 +32,11 @@ brute-force loops, closed forms, library routines (scipy's logsumexp) and
 the numbers the pages print; see that file's header for the map.
 """
 from .dense import attention, attention_heads
+from .rope import axis_split, grid_positions, angles, rotate, round_bf16, rope, rope_bf16
 from .vsa import (CUBE, geometry, cube_layout, pool, coarse_scores, select_topk,
                   near_tie_tolerance, fine, vsa, coarse_output, gated, flops_fine, kv_stream_bytes)
 
 __all__ = ["attention", "attention_heads", "CUBE", "geometry", "cube_layout", "pool",
            "coarse_scores", "select_topk", "near_tie_tolerance", "fine", "vsa",
-           "coarse_output", "gated", "flops_fine", "kv_stream_bytes"]
+           "coarse_output", "gated", "flops_fine", "kv_stream_bytes", "axis_split", "grid_positions",
+           "angles", "rotate", "round_bf16", "rope", "rope_bf16"]

@@ -25,6 +25,14 @@ Map of pins (function -> what fixes it):
   means; a one-cube grid gives the mean of V; gate = 0 gives the fine output
   exactly; the merge is linear in the gate.
 * oracle.flops_fine / kv_stream_bytes: the page's 3.35 TFLOP and 64 GB.
+* oracle.rope (3D RoPE, adopted definition): closed forms on D = 6 (angles
+  are exactly t, h, w radians) and D = 12 (second pair at theta**-0.5); a
+  Python loop over complex numbers on a ragged grid; position 0 is the
+  identity; pair norms are kept; dot products depend only on the position
+  difference; each axis part moves only with its own coordinate.
+* oracle.round_bf16: matches the float32 round-to-nearest-even of synth on
+  float32-representable values, resolves exact ties to even, and rounds fp64
+  values just above a tie upward (where an fp32 intermediate would not).
 """
 import json
 import math
@@ -35,6 +43,7 @@ import pytest
 from scipy.special import logsumexp
 
 import oracle
+import synth
 
 
 
@@ -478,3 +487,87 @@ def test_gate_zero_and_linearity():
     d2 = oracle.gated(q, k, v, tok, idx, s, g2)[0] - of
     d12 = oracle.gated(q, k, v, tok, idx, s, g1 + g2)[0] - of
     np.testing.assert_allclose(d12, d1 + d2, atol=1e-12)
+
+
+# --------------------------------------------------------------- 3D RoPE
+
+def test_rope_closed_form_d6():
+    """D = 6: one pair per axis, frequency theta**0 = 1, so the angles are t, h, w radians."""
+    x = np.tile([1.0, 0.0, 1.0, 0.0, 1.0, 0.0], (2 * 3 * 4, 1))
+    r = oracle.rope(x, 2, 3, 4)
+    t, h, w = 1, 2, 3
+    n = (t * 3 + h) * 4 + w
+    expect = [math.cos(t), math.sin(t), math.cos(h), math.sin(h), math.cos(w), math.sin(w)]
+    np.testing.assert_allclose(r[n], expect, atol=1e-15)
+    # a pair (0, 1) turns to (-sin, cos)
+    y = np.tile([0.0, 1.0, 0.0, 1.0, 0.0, 1.0], (24, 1))
+    np.testing.assert_allclose(oracle.rope(y, 2, 3, 4)[n], [-math.sin(1), math.cos(1), -math.sin(2),
+                                                             math.cos(2), -math.sin(3), math.cos(3)], atol=1e-15)
+
+
+def test_rope_closed_form_d12_second_frequency():
+    """D = 12: parts of 4 dims, two pairs each, frequencies 1 and theta**(-2/4) = 0.01."""
+    assert oracle.axis_split(12) == (4, 4, 4)
+    x = np.zeros((5 * 1 * 1, 12))
+    x[:, 2] = 1.0                                  # pair 1 of the t part
+    r = oracle.rope(x, 5, 1, 1)
+    np.testing.assert_allclose(r[3, 2:4], [math.cos(0.03), math.sin(0.03)], atol=1e-15)
+    assert oracle.axis_split(128) == (44, 42, 42) and oracle.axis_split(64) == (24, 20, 20)
+
+
+def test_rope_loop_brute_force_ragged_grid():
+    T, H, W, D, theta = 3, 5, 7, 20, 500.0
+    x = rng(60).normal(size=(T * H * W, D))
+    r = oracle.rope(x, T, H, W, theta)
+    dt, dh, dw = D - 4 * (D // 6), 2 * (D // 6), 2 * (D // 6)
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                n = (t * H + h) * W + w
+                start = 0
+                for pos, d_a in ((t, dt), (h, dh), (w, dw)):
+                    for i in range(d_a // 2):
+                        z = complex(x[n, start + 2 * i], x[n, start + 2 * i + 1])
+                        z *= complex(math.cos(pos * math.pow(theta, -2.0 * i / d_a)),
+                                     math.sin(pos * math.pow(theta, -2.0 * i / d_a)))
+                        assert abs(r[n, start + 2 * i] - z.real) < 1e-12
+                        assert abs(r[n, start + 2 * i + 1] - z.imag) < 1e-12
+                    start += d_a
+                assert start == D
+
+
+def test_rope_invariants():
+    T, H, W, D = 4, 6, 5, 128
+    x = rng(61).normal(size=(T * H * W, D))
+    r = oracle.rope(x, T, H, W)
+    np.testing.assert_array_equal(r[0], x[0])       # position (0, 0, 0): identity
+    np.testing.assert_allclose(r[:, 0::2] ** 2 + r[:, 1::2] ** 2, x[:, 0::2] ** 2 + x[:, 1::2] ** 2,
+                               rtol=1e-12)          # each pair keeps its length
+    # the q.k product depends only on the position difference
+    q, k = rng(62).normal(size=(1, D)), rng(63).normal(size=(1, D))
+    def dot(p, pp):
+        rq = oracle.rotate(q, oracle.angles(np.array([p]), D))
+        rk = oracle.rotate(k, oracle.angles(np.array([pp]), D))
+        return float((rq * rk).sum())
+    for p, pp, s in (((3, 1, 4), (0, 2, 2), (5, 7, 9)), ((0, 0, 0), (1, 1, 1), (20, 3, 11))):
+        shifted = tuple(a + b for a, b in zip(p, s)), tuple(a + b for a, b in zip(pp, s))
+        assert abs(dot(p, pp) - dot(*shifted)) < 1e-10
+    assert abs(dot((3, 1, 4), (0, 2, 2)) - dot((3, 1, 4), (0, 2, 3))) > 1e-3
+    # each axis part moves with its own coordinate only
+    dt, dh, dw = oracle.axis_split(D)
+    a = oracle.angles(np.array([[2, 3, 4], [2, 5, 4]]), D)
+    assert (a[0, :dt // 2] == a[1, :dt // 2]).all() and (a[0, (dt + dh) // 2:] == a[1, (dt + dh) // 2:]).all()
+    assert (a[0, dt // 2:(dt + dh) // 2] != a[1, dt // 2:(dt + dh) // 2]).all()
+
+
+def test_round_bf16():
+    x32 = (rng(64).normal(size=10000) * np.exp(rng(65).uniform(-20, 20, size=10000))).astype(np.float32)
+    np.testing.assert_array_equal(oracle.round_bf16(x32.astype(np.float64)),
+                                  synth.bits_to_f64(synth.bf16_bits(x32)))
+    one = 1.0
+    assert oracle.round_bf16(np.array([one + 2.0 ** -8]))[0] == 1.0                      # tie: to even
+    assert oracle.round_bf16(np.array([one + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6      # tie: to even
+    assert oracle.round_bf16(np.array([-(one + 2.0 ** -8)]))[0] == -1.0
+    # just above a tie only in fp64: rounds up (an fp32 intermediate would land on the tie)
+    assert oracle.round_bf16(np.array([one + 2.0 ** -8 + 2.0 ** -40]))[0] == 1.0 + 2.0 ** -7
+    assert oracle.round_bf16(np.array([0.0]))[0] == 0.0
