@@ -278,6 +278,43 @@ def main():
         wf.profile_enable(False)
         del gate
 
+    # extra record (not part of the step): 3D RoPE of Q and K, standalone (wf_rope_qk, the form dense
+    # attention takes) and fused into VSA's gather (the coarse stage with RoPE, then the fine stage)
+    rope = None
+    if not args.no_extra:
+        qr, kr = torch.empty_like(qv), torch.empty_like(kv)
+
+        def rope_runs():
+            wf.wf_rope_qk(qv, kv, grid, q_out=qr, k_out=kr)
+            wf.wf_rope_qk(qv, kv, grid, precision=64, q_out=qr, k_out=kr)
+            wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v, rope_theta=10000.0)
+            wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
+
+        rope_runs()
+        torch.cuda.synchronize()
+        wf.profile_enable(True)
+        for _ in range(max(3, args.steps // 2)):
+            rope_runs()
+        torch.cuda.synchronize()
+        rk = {}
+        for name in ("wf_rope_qk", "wf_rope_qk_fp64", "wf_vsa_gather_rope", "wf_vsa_scores", "wf_vsa_topk",
+                     "wf_vsa_fine"):
+            n, tot = wf.profile_query(name)
+            rk[name] = tot / n
+        wf.profile_enable(False)
+        rope_bytes = 4.0 * wv.B * wv.Hh * wv.N * wv.D * 2   # Q and K, read and written
+        rope = {"theta": 10000.0, "precision_fused_and_rope_qk": 32,
+                "rope_qk_ms": rk["wf_rope_qk"],
+                "rope_qk_gbs": rope_bytes / (rk["wf_rope_qk"] * 1e-3) / 1e9,
+                "rope_qk_frac_hbm": rope_bytes / (rk["wf_rope_qk"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "rope_qk_fp64_ms": rk["wf_rope_qk_fp64"],
+                "rope_qk_fp64_frac_hbm": rope_bytes / (rk["wf_rope_qk_fp64"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "vsa_ms_per_call_fused_rope": rk["wf_vsa_gather_rope"] + rk["wf_vsa_scores"] + rk["wf_vsa_topk"] + rk["wf_vsa_fine"],
+                "gather_rope_ms": rk["wf_vsa_gather_rope"],
+                "fused_rope_extra_ms": rk["wf_vsa_gather_rope"] - kern["wf_vsa_gather"],
+                "kernel_ms": rk}
+        del qr, kr
+
     # extra record (not part of the step): one GPU's share of the heads when 8 GPUs split them
     # (5 of 40 per CFG branch): the same kernels at Hh = 5 and full N
     share = None
@@ -389,6 +426,7 @@ def main():
             "merge_extra_ms": gated_ms["wf_vsa_fine_gated"] - kern["wf_vsa_fine"],
             "merge_extra_floor_ms": by_v["merge"] / PEAK_HBM_GBS / 1e6,
         },
+        "rope": rope,
         "vsa_k78": None if k78_ms is None else {
             "topk": k78,
             "ms_per_call": sum(k78_ms.values()),

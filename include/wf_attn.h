@@ -178,6 +178,57 @@ int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t
                           int32_t D, float scale, int32_t topk, float* o, float* lse,
                           float* o_coarse, void* stream);
 
+/* ------------------------------------------------------ 3D RoPE */
+
+/*
+ * 3D rotary position embedding of Q and K.  "推理优化" (Inference
+ * optimization, WorldFoundry docs), section "Exact or numerically equivalent
+ * Wan kernels", entry fused_rope, names a fused 3D RoPE whose rotation runs in
+ * fp32 or fp64 but gives no frequencies; the library takes the common
+ * Wan-style definition and offers both precisions:
+ *   - the head dimension is cut into consecutive parts of D - 4*floor(D/6),
+ *     2*floor(D/6) and 2*floor(D/6) dims for the t, h and w axes
+ *     (D = 128: 44, 42, 42; D = 64: 24, 20, 20);
+ *   - inside a part of d_a dims, elements (2i, 2i+1) form pair i and rotate by
+ *     phi = pos * theta^(-2i/d_a), pos being the token's 0-based coordinate
+ *     on that axis: (x0, x1) -> (x0 cos phi - x1 sin phi, x0 sin phi + x1 cos phi);
+ *   - precision 64: the rotation is computed in fp64 and rounded once to
+ *     bf16 (nearest, ties to even); a result below the normal bf16 range
+ *     (|y| < 2^-126, which rotated inputs of normal size never reach)
+ *     becomes a signed zero;
+ *   - precision 32: cos and sin (taken in fp64) are rounded to fp32, each
+ *     product and sum is rounded to fp32 (no fused multiply-add), and that
+ *     fp32 value is rounded to bf16 (nearest, ties to even).  About 3x less
+ *     arithmetic; it differs from precision 64 by one bf16 step on a small
+ *     fraction of near-tie elements.
+ *
+ *   q, k           bf16 [B][Hh][T*H*W][D], read.
+ *   q_out, k_out   bf16, same shape, written.  Each may be the same pointer
+ *                  as its input (in place); otherwise no two of the four
+ *                  buffers may overlap.
+ *   D              64 or 128.   theta: finite, > 0 (Wan uses 10000).
+ *   precision      32 or 64.
+ */
+int32_t wf_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int32_t B, int32_t Hh,
+                   int32_t T, int32_t H, int32_t W, int32_t D, double theta, int32_t precision,
+                   void* stream);
+
+/*
+ * wf_vsa_coarse_topk with the 3D RoPE of wf_rope_qk (frequency base
+ * rope_theta, finite and > 0; rope_precision 32 or 64) applied to Q and K
+ * inside the gather, so the
+ * rotation costs no separate pass over Q and K.  Cube means, scores, the plan
+ * and the fine stage (wf_vsa_fine, wf_vsa_fine_gated, which read the gathered
+ * Q and K from the workspace) all see the rotated vectors; the result equals
+ * wf_rope_qk followed by wf_vsa_coarse_topk bit for bit.  Arguments otherwise
+ * as for wf_vsa_coarse_topk.
+ */
+int32_t wf_vsa_coarse_topk_rope(const void* q, const void* k, const void* v,
+                                int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                                float scale, int32_t topk, double rope_theta,
+                                int32_t rope_precision, int32_t* idx, float* coarse_scores,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------ per-kernel timing */
 
 /*

@@ -18,9 +18,13 @@ own terms in tests/test_oracle.py:
    0-based coordinate on that axis and theta the frequency base (10000).
 3. A pair (x0, x1) rotated by phi becomes
    (x0 cos phi - x1 sin phi, x0 sin phi + x1 cos phi).
-4. Q and K are rotated, V is not; the rotation is computed in fp64 (the
-   page's fp64 option) and the result is rounded to bf16, round to nearest
-   even, since attention consumes bf16 Q and K.
+4. Q and K are rotated, V is not, and the result is rounded to bf16, round
+   to nearest even, since attention consumes bf16 Q and K.  The page's two
+   precisions are both defined: "fp64" rotates in fp64 arithmetic; "fp32"
+   rounds cos and sin (taken in fp64) to fp32 and then forms
+   x0*c - x1*s and x0*s + x1*c with each product and the sum rounded to fp32
+   (no fused multiply-add), so the bf16 rounding decision is taken on that
+   fp32 value.
 """
 from __future__ import annotations
 
@@ -50,12 +54,21 @@ def angles(pos: np.ndarray, D: int, theta: float = 10000.0) -> np.ndarray:
     return np.concatenate(cols, axis=1)
 
 
-def rotate(x: np.ndarray, phi: np.ndarray) -> np.ndarray:
-    """Rotate the pairs (x[:, 2i], x[:, 2i+1]) of x [N, D] by phi [N, D/2] (definition 3)."""
-    x0, x1 = x[:, 0::2], x[:, 1::2]
-    c, s = np.cos(phi), np.sin(phi)
-    out = np.empty_like(x, dtype=np.float64)
-    out[:, 0::2] = x0 * c - x1 * s
+def rotate(x: np.ndarray, phi: np.ndarray, precision: str = "fp64") -> np.ndarray:
+    """Rotate the pairs (x[:, 2i], x[:, 2i+1]) of x [N, D] by phi [N, D/2] (definitions 3, 4).
+
+    Returns float64; with precision "fp32" every value is an fp32 result.
+    """
+    if precision == "fp64":
+        x0, x1 = x[:, 0::2], x[:, 1::2]
+        c, s = np.cos(phi), np.sin(phi)
+    elif precision == "fp32":
+        x0, x1 = x[:, 0::2].astype(np.float32), x[:, 1::2].astype(np.float32)
+        c, s = np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
+    else:
+        raise ValueError("precision is 'fp64' or 'fp32'")
+    out = np.empty(x.shape, dtype=np.float64)
+    out[:, 0::2] = x0 * c - x1 * s      # float32 operands: each step rounds to fp32
     out[:, 1::2] = x0 * s + x1 * c
     return out
 
@@ -71,13 +84,15 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return np.ldexp(np.rint(m * 256.0), e - 8)
 
 
-def rope(x: np.ndarray, T: int, H: int, W: int, theta: float = 10000.0) -> np.ndarray:
-    """x [N, D] (N = T*H*W, row-major (t, h, w)) rotated in fp64, not rounded."""
+def rope(x: np.ndarray, T: int, H: int, W: int, theta: float = 10000.0,
+         precision: str = "fp64") -> np.ndarray:
+    """x [N, D] (N = T*H*W, row-major (t, h, w)) rotated, not rounded to bf16."""
     if x.shape[0] != T * H * W:
         raise ValueError("x must hold the T*H*W tokens of the grid")
-    return rotate(x, angles(grid_positions(T, H, W), x.shape[1], theta))
+    return rotate(x, angles(grid_positions(T, H, W), x.shape[1], theta), precision)
 
 
-def rope_bf16(x: np.ndarray, T: int, H: int, W: int, theta: float = 10000.0) -> np.ndarray:
-    """What attention consumes: the fp64 rotation of x rounded to bf16 (definition 4)."""
-    return round_bf16(rope(x, T, H, W, theta))
+def rope_bf16(x: np.ndarray, T: int, H: int, W: int, theta: float = 10000.0,
+              precision: str = "fp64") -> np.ndarray:
+    """What attention consumes: the rotation of x rounded to bf16 (definition 4)."""
+    return round_bf16(rope(x, T, H, W, theta, precision))

@@ -25,7 +25,7 @@ def wf():
 def test_every_declared_symbol_is_exported(wf):
     names = declared_functions()
     assert "wf_attn_dense" in names and "wf_vsa_coarse_topk" in names and "wf_vsa_fine" in names
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(wf.lib, n), f"{n} declared in wf_attn.h but not exported"
 
@@ -102,6 +102,18 @@ def test_vsa_argument_errors(wf):
     assert fine(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 0, FAKE, None, None) == 1
     assert fine(FAKE, 10, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None) == 3
     assert fine(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, float("inf"), 3, FAKE, None, None) == 1
+    rope = wf.lib.wf_rope_qk
+    assert rope(FAKE, FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.0, 32, None) == 1
+    assert rope(FAKE, FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 96, 1e4, 32, None) == 2
+    assert rope(None, FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 1e4, 32, None) == 1
+    assert rope(FAKE, FAKE, FAKE + 2, FAKE, 1, 2, 5, 6, 7, 128, 1e4, 32, None) == 1
+    assert rope(FAKE, FAKE, FAKE, FAKE, 1, 2, 0, 6, 7, 128, 1e4, 32, None) == 1
+    assert rope(FAKE, FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 1e4, 16, None) == 1
+    cr = wf.lib.wf_vsa_coarse_topk_rope
+    assert cr(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, float("inf"), 32, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert cr(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, -1.0, 32, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert cr(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 9, 1e4, 32, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert cr(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 1e4, 48, FAKE, None, FAKE, 1 << 30, None) == 1
     gated = wf.lib.wf_vsa_fine_gated
     assert gated(FAKE, 1 << 30, FAKE, None, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1
     assert gated(FAKE, 1 << 30, FAKE, FAKE + 4, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1

@@ -30,6 +30,10 @@ Map of pins (function -> what fixes it):
   Python loop over complex numbers on a ragged grid; position 0 is the
   identity; pair norms are kept; dot products depend only on the position
   difference; each axis part moves only with its own coordinate.
+* oracle.rope, precision "fp32": every output is an fp32 value, within a few
+  fp32 rounding steps of the fp64 rotation, and its bf16 rounding agrees
+  with the fp64 mode's except on a sliver of near-ties (never by more than
+  one bf16 step).
 * oracle.round_bf16: matches the float32 round-to-nearest-even of synth on
   float32-representable values, resolves exact ties to even, and rounds fp64
   values just above a tie upward (where an fp32 intermediate would not).
@@ -571,3 +575,21 @@ def test_round_bf16():
     # just above a tie only in fp64: rounds up (an fp32 intermediate would land on the tie)
     assert oracle.round_bf16(np.array([one + 2.0 ** -8 + 2.0 ** -40]))[0] == 1.0 + 2.0 ** -7
     assert oracle.round_bf16(np.array([0.0]))[0] == 0.0
+
+
+def test_rope_fp32_mode():
+    T, H, W, D = 5, 7, 9, 128
+    x = synth.bits_to_f64(synth.bf16_bits(rng(66).normal(size=(T * H * W, D)).astype(np.float32)))
+    r64 = oracle.rope(x, T, H, W)
+    r32 = oracle.rope(x, T, H, W, precision="fp32")
+    np.testing.assert_array_equal(r32.astype(np.float32).astype(np.float64), r32)   # fp32 values
+    # two products (each off by <= 1/2 ulp, plus the cos/sin rounding) and one sum: a few fp32 ulps
+    scale = np.abs(x).max()
+    assert np.abs(r32 - r64).max() <= 4 * 2.0 ** -24 * 2 * scale
+    b64, b32 = oracle.round_bf16(r64), oracle.round_bf16(r32)
+    differ = b64 != b32
+    assert differ.mean() < 1e-3
+    step = np.ldexp(1.0, np.frexp(np.abs(b64[differ]))[1] - 8)         # one bf16 step at that size
+    assert (np.abs(b64[differ] - b32[differ]) <= step * 1.0000001).all()
+    with pytest.raises(ValueError):
+        oracle.rope(x, T, H, W, precision="fp16")

@@ -35,6 +35,10 @@ _SIGS = {
     "wf_vsa_fine": (_i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp]),
     "wf_vsa_fine_gated": (_i32, [_vp, _sz, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                  _vp, _vp, _vp, _vp]),
+    "wf_rope_qk": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_double, _i32,
+                          _vp]),
+    "wf_vsa_coarse_topk_rope": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                       ctypes.c_double, _i32, _vp, _vp, _vp, _sz, _vp]),
     "wf_profile_enable": (_i32, [_i32]),
     "wf_profile_query": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
                                 ctypes.POINTER(ctypes.c_double)]),
@@ -121,9 +125,32 @@ def wf_attn_dense(q, k, v, scale: Optional[float] = None, with_lse: bool = False
     return out, lse
 
 
+def wf_rope_qk(q, k, grid, theta: float = 10000.0, precision: int = 32, q_out=None, k_out=None):
+    """3D RoPE of q and k through wf_rope_qk (precision 32 or 64).  Returns (q_rot, k_rot), bf16.
+
+    Pass q_out=q, k_out=k to rotate in place.
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 CUDA tensor [B, Hh, N, D]")
+    if q.shape != k.shape:
+        raise ValueError(f"q, k shapes differ: {tuple(q.shape)} {tuple(k.shape)}")
+    T, H, W = grid
+    B, Hh, N, D = q.shape
+    if N != T * H * W:
+        raise ValueError(f"N = {N} but the grid has {T * H * W} tokens")
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _check(lib.wf_rope_qk(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, Hh, T, H, W, D,
+                          float(theta), int(precision), _stream_handle(q.device)), "wf_rope_qk")
+    return q_out, k_out
+
+
 def wf_vsa_coarse_topk(q, k, v, grid, topk: int, scale: Optional[float] = None,
-                       with_scores: bool = False, idx=None, scores=None, workspace=None):
-    """VSA coarse stage through wf_vsa_coarse_topk.
+                       with_scores: bool = False, idx=None, scores=None, workspace=None,
+                       rope_theta: Optional[float] = None, rope_precision: int = 32):
+    """VSA coarse stage through wf_vsa_coarse_topk (wf_vsa_coarse_topk_rope when rope_theta is given).
 
     grid = (T, H, W).  Returns (idx int32 [B,Hh,C,topk], scores or None,
     workspace) -- pass the workspace on to wf_vsa_fine.
@@ -141,10 +168,17 @@ def wf_vsa_coarse_topk(q, k, v, grid, topk: int, scale: Optional[float] = None,
     if with_scores and scores is None:
         scores = torch.empty((B, Hh, C, C), dtype=torch.float32, device=q.device)
     ws = _workspace(vsa_workspace_bytes(B, Hh, T, H, W, D), q.device, workspace)
-    _check(lib.wf_vsa_coarse_topk(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D, scale,
-                                  topk, idx.data_ptr(), _ptr(scores), ws.data_ptr(),
-                                  ws.numel() * ws.element_size(), _stream_handle(q.device)),
-           "wf_vsa_coarse_topk")
+    if rope_theta is None:
+        _check(lib.wf_vsa_coarse_topk(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D, scale,
+                                      topk, idx.data_ptr(), _ptr(scores), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream_handle(q.device)),
+               "wf_vsa_coarse_topk")
+    else:
+        _check(lib.wf_vsa_coarse_topk_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D,
+                                           scale, topk, float(rope_theta), int(rope_precision),
+                                           idx.data_ptr(), _ptr(scores),
+                                           ws.data_ptr(), ws.numel() * ws.element_size(),
+                                           _stream_handle(q.device)), "wf_vsa_coarse_topk_rope")
     return idx, scores, ws
 
 

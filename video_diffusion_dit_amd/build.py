@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwfattn.so")
-SOURCES = ["capi.hip", "dense.hip", "vsa.hip"]
+SOURCES = ["capi.hip", "dense.hip", "vsa.hip", "rope.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU instructions.

@@ -181,10 +181,11 @@ size_t wf_vsa_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32
   return wf::vsa_layout(B * Hh, T, H, W, D).total;
 }
 
-int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v, int32_t B, int32_t Hh,
-                           int32_t T, int32_t H, int32_t W, int32_t D, float scale, int32_t topk,
-                           int32_t* idx, float* coarse_scores, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+static int32_t vsa_coarse(const void* q, const void* k, const void* v, int32_t B, int32_t Hh,
+                          int32_t T, int32_t H, int32_t W, int32_t D, float scale, int32_t topk,
+                          double rope_theta, int32_t rope_precision, int32_t* idx,
+                          float* coarse_scores, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   WF_CHECK_PTR(q);
   WF_CHECK_PTR(k);
   WF_CHECK_PTR(v);
@@ -200,9 +201,55 @@ int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v, int32_t 
     return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
                 need);
   WF_CHECK_PTR(workspace);
-  hipError_t e = wf::launch_vsa_coarse(q, k, v, B * Hh, T, H, W, D, scale, topk, idx, coarse_scores,
-                                       workspace, static_cast<hipStream_t>(stream));
+  hipError_t e = wf::launch_vsa_coarse(q, k, v, B * Hh, T, H, W, D, scale, topk, rope_theta,
+                                       rope_precision, idx, coarse_scores, workspace,
+                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "VSA coarse launch");
+  return ok();
+}
+
+int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v, int32_t B, int32_t Hh,
+                           int32_t T, int32_t H, int32_t W, int32_t D, float scale, int32_t topk,
+                           int32_t* idx, float* coarse_scores, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return vsa_coarse(q, k, v, B, Hh, T, H, W, D, scale, topk, 0.0, 0, idx, coarse_scores, workspace,
+                    workspace_bytes, stream);
+}
+
+int32_t wf_vsa_coarse_topk_rope(const void* q, const void* k, const void* v, int32_t B, int32_t Hh,
+                                int32_t T, int32_t H, int32_t W, int32_t D, float scale,
+                                int32_t topk, double rope_theta, int32_t rope_precision,
+                                int32_t* idx, float* coarse_scores, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!isfinite(rope_theta) || !(rope_theta > 0.0))
+    return fail(WF_ERR_INVALID_ARG, "rope_theta %g must be finite and > 0", rope_theta);
+  if (rope_precision != 32 && rope_precision != 64)
+    return fail(WF_ERR_INVALID_ARG, "rope_precision %d (32 or 64)", rope_precision);
+  return vsa_coarse(q, k, v, B, Hh, T, H, W, D, scale, topk, rope_theta, rope_precision, idx,
+                    coarse_scores, workspace, workspace_bytes, stream);
+}
+
+int32_t wf_rope_qk(const void* q, const void* k, void* q_out, void* k_out, int32_t B, int32_t Hh,
+                   int32_t T, int32_t H, int32_t W, int32_t D, double theta, int32_t precision,
+                   void* stream) {
+  WF_CHECK_PTR(q);
+  WF_CHECK_PTR(k);
+  WF_CHECK_PTR(q_out);
+  WF_CHECK_PTR(k_out);
+  if (T < 1 || H < 1 || W < 1) return fail(WF_ERR_INVALID_ARG, "bad grid T=%d H=%d W=%d", T, H, W);
+  const long long N = (long long)T * H * W;
+  if (!sizes_ok(B, Hh, N, D))
+    return fail(WF_ERR_INVALID_ARG, "bad sizes B=%d Hh=%d N=%lld D=%d", B, Hh, N, D);
+  if (D != 64 && D != 128) return fail(WF_ERR_UNSUPPORTED, "RoPE head dimension %d (64 or 128)", D);
+  if ((long long)B * T * H * ((W + 63) / 64) * ((Hh + 7) / 8) >= (1ll << 31))
+    return fail(WF_ERR_UNSUPPORTED, "grid %dx%dx%d with B=%d Hh=%d: too many workgroups", T, H, W, B, Hh);
+  if (!isfinite(theta) || !(theta > 0.0))
+    return fail(WF_ERR_INVALID_ARG, "theta %g must be finite and > 0", theta);
+  if (precision != 32 && precision != 64)
+    return fail(WF_ERR_INVALID_ARG, "precision %d (32 or 64)", precision);
+  hipError_t e = wf::launch_rope_qk(q, k, q_out, k_out, B, Hh, T, H, W, D, theta, precision,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "RoPE launch");
   return ok();
 }
 

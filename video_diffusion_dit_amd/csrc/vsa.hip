@@ -9,6 +9,7 @@
 // ms target" counts one output tile per (query cube, head).
 #include "wf_device.hpp"
 #include "wf_launch.hpp"
+#include "wf_rope.hpp"
 
 namespace wf {
 
@@ -54,22 +55,44 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 // over the cube's real tokens, and the fp32 mean of V split into two bf16
 // parts, hi = bf16(mean) and lo = bf16(mean - hi), at key cube c of the
 // operand-ordered means (vbar_index; key cubes C..Cs-1 are zeroed, so the
-// coarse-branch product may run over whole 32-wide steps).
-template <int D>
+// coarse-branch product may run over whole 32-wide steps).  With ROPE, Q and
+// K are rotated by the 3D RoPE (wf_rope.hpp) on the way in, so everything
+// downstream (cube means, scores, the fine stage) sees the rotated vectors;
+// the cube's 4 t, 4 h and 4 w coordinates need one table of 4*(t2+h2+w2)
+// (cos, sin) pairs, one fp64 sincos per thread.  ROPE is the rotation's
+// precision (32 or 64), 0 for none.
+template <int D, int ROPE>
 __global__ void __launch_bounds__(256) wf_vsa_gather(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ qc, uint16_t* __restrict__ kc, uint16_t* __restrict__ vct,
-    float* __restrict__ qbar, float* __restrict__ kbar, uint16_t* __restrict__ vbt, Grid3 g) {
+    float* __restrict__ qbar, float* __restrict__ kbar, uint16_t* __restrict__ vbt, Grid3 g,
+    double theta) {
   constexpr int ROWCH = D / 8;            // 16-byte chunks per row
   constexpr int RSTEP = 256 / ROWCH;      // rows covered by one pass of the workgroup
   constexpr int VSTR = D + 2;
+  constexpr RopeSplit sp = rope_split(D);
+  constexpr int NTAB = ROPE ? 4 * (sp.t2 + sp.h2 + sp.w2) : 1;
+  using CS = RopeCS<ROPE == 64 ? 64 : 32>;
   __shared__ float red[RSTEP][D];
   __shared__ uint16_t vtile[64 * VSTR];
+  __shared__ CS tab[NTAB];
   const int tid = threadIdx.x, c16 = tid % ROWCH, r0 = tid / ROWCH;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / g.C, c = item % g.C;
   int ct, ch, cw;
   cube_coords(g, c, ct, ch, cw);
+  if constexpr (ROPE != 0) {  // [4 t][t2] then [4 h][h2] then [4 w][w2]
+    for (int e = tid; e < NTAB; e += 256) {
+      if (e < 4 * sp.t2)
+        tab[e] = rope_cs<CS>(4 * ct + e / sp.t2, rope_freq(e % sp.t2, 2 * sp.t2, theta));
+      else if (e < 4 * (sp.t2 + sp.h2))
+        tab[e] = rope_cs<CS>(4 * ch + (e - 4 * sp.t2) / sp.h2, rope_freq((e - 4 * sp.t2) % sp.h2, 2 * sp.h2, theta));
+      else
+        tab[e] = rope_cs<CS>(4 * cw + (e - 4 * (sp.t2 + sp.h2)) / sp.w2,
+                             rope_freq((e - 4 * (sp.t2 + sp.h2)) % sp.w2, 2 * sp.w2, theta));
+    }
+    __syncthreads();
+  }
   const long N = (long)g.T * g.H * g.W;
   const long cube_row0 = ((long)bh * g.C + c) * 64;
   const int count = min(4, g.T - 4 * ct) * min(4, g.H - 4 * ch) * min(4, g.W - 4 * cw);
@@ -83,6 +106,16 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       const int tok = slot_token(g, ct, ch, cw, s);
       uint4 u = make_uint4(0, 0, 0, 0);
       if (tok >= 0) u = *reinterpret_cast<const uint4*>(src + (long)tok * D + c16 * 8);
+      if constexpr (ROPE != 0) {
+        if (which < 2 && tok >= 0) {
+          const int st = s >> 4, sh = (s >> 2) & 3, sw = s & 3;
+          u = rope_rotate_chunk(u, c16 * 4, [&](int p) {
+            return p < sp.t2 ? tab[st * sp.t2 + p]
+                 : p < sp.t2 + sp.h2 ? tab[4 * sp.t2 + sh * sp.h2 + (p - sp.t2)]
+                                     : tab[4 * (sp.t2 + sp.h2) + sw * sp.w2 + (p - sp.t2 - sp.h2)];
+          });
+        }
+      }
       const uint16_t* e = reinterpret_cast<const uint16_t*>(&u);
       if (which < 2) {
         uint16_t* dst = (which == 0 ? qc : kc) + (cube_row0 + s) * D + c16 * 8;
@@ -518,8 +551,8 @@ VsaLayout vsa_layout(int BH, int T, int H, int W, int D) {
 }
 
 hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH, int T, int H,
-                             int W, int D, float scale, int topk, int* idx, float* scores_out,
-                             void* ws, hipStream_t s) {
+                             int W, int D, float scale, int topk, double rope_theta,
+                             int rope_precision, int* idx, float* scores_out, void* ws, hipStream_t s) {
   const Grid3 g = make_grid(T, H, W);
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   char* w = static_cast<char*>(ws);
@@ -529,11 +562,18 @@ hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH
   auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
   auto sc = reinterpret_cast<float*>(w + L.scores);
   auto stat = reinterpret_cast<float2*>(w + L.stat);
-  hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
-    hipLaunchKernelGGL(wf_vsa_gather<128>, dim3((unsigned)(BH * g.C)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), qc, kc, vct, qbar, kbar, vbt, g);
-  });
+  auto gather = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(256), 0, s, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qc, kc, vct, qbar,
+                       kbar, vbt, g, rope_theta);
+  };
+  hipError_t e;
+  if (rope_theta > 0.0 && rope_precision == 64)
+    e = wf_launch("wf_vsa_gather_rope_fp64", s, [&] { gather(wf_vsa_gather<128, 64>); });
+  else if (rope_theta > 0.0)
+    e = wf_launch("wf_vsa_gather_rope", s, [&] { gather(wf_vsa_gather<128, 32>); });
+  else
+    e = wf_launch("wf_vsa_gather", s, [&] { gather(wf_vsa_gather<128, 0>); });
   if (e != hipSuccess) return e;
   const int nt = (g.C + 63) / 64;
   e = wf_launch("wf_vsa_scores", s, [&] {

@@ -20,6 +20,10 @@ hipError_t wf_launch(const char* name, hipStream_t s, F&& launch) {
   return e;
 }
 
+// 3D RoPE of Q and K (bf16 [B][Hh][T*H*W][D], D = 64 or 128), precision 32 or 64; out may equal in.
+hipError_t launch_rope_qk(const void* q, const void* k, void* qo, void* ko, int B, int Hh, int T, int H,
+                          int W, int D, double theta, int precision, hipStream_t s);
+
 // Dense attention.
 size_t dense_workspace_bytes(int BH, int N, int D);
 hipError_t launch_dense(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
@@ -31,9 +35,11 @@ struct VsaLayout {
   size_t qc, kc, vct, qbar, kbar, vbt, scores, stat, ocoarse, flag, total;
 };
 VsaLayout vsa_layout(int BH, int T, int H, int W, int D);
+// rope_theta > 0: Q and K pass through the 3D RoPE with that frequency base in the gather,
+// rotated in fp32 or fp64 (rope_precision 32 or 64).
 hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH, int T, int H,
-                             int W, int D, float scale, int topk, int* idx, float* scores_out,
-                             void* ws, hipStream_t s);
+                             int W, int D, float scale, int topk, double rope_theta,
+                             int rope_precision, int* idx, float* scores_out, void* ws, hipStream_t s);
 hipError_t launch_vsa_check(const int* idx, int BH, int C, int topk, void* ws, size_t flag_off,
                             hipStream_t s, int* bad);
 hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H, int W, int D,
