@@ -315,6 +315,32 @@ def main():
                 "kernel_ms": rk}
         del qr, kr
 
+    # extra record (not part of the step): the softmax reference policies on the step's dense and
+    # VSA fine kernels -- guarded integer reference (the default), running max, fixed first tile
+    policies = None
+    if not args.no_extra:
+        wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
+        pk = {}
+        for mode, tag in ((1, "_running_max"), (2, "_fixed_first"), (0, "")):
+            wf.wf_attn_dense(qd, kd, vd, out=od, workspace=ws_d, softmax_mode=mode)
+            wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov, softmax_mode=mode)
+            torch.cuda.synchronize()
+            wf.profile_enable(True)
+            for _ in range(3):
+                wf.wf_attn_dense(qd, kd, vd, out=od, workspace=ws_d, softmax_mode=mode)
+                for _ in range(4):
+                    wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov, softmax_mode=mode)
+            torch.cuda.synchronize()
+            for name in ("wf_dense_fwd" + tag, "wf_vsa_fine" + tag):
+                n, tot = wf.profile_query(name)
+                pk[name] = tot / n
+            wf.profile_enable(False)
+        policies = {"kernel_ms": pk,
+                    "dense_running_max_over_guarded": pk["wf_dense_fwd_running_max"] / pk["wf_dense_fwd"],
+                    "dense_fixed_first_over_guarded": pk["wf_dense_fwd_fixed_first"] / pk["wf_dense_fwd"],
+                    "vsa_fine_running_max_over_guarded": pk["wf_vsa_fine_running_max"] / pk["wf_vsa_fine"],
+                    "vsa_fine_fixed_first_over_guarded": pk["wf_vsa_fine_fixed_first"] / pk["wf_vsa_fine"]}
+
     # extra record (not part of the step): one GPU's share of the heads when 8 GPUs split them
     # (5 of 40 per CFG branch): the same kernels at Hh = 5 and full N
     share = None
@@ -427,6 +453,7 @@ def main():
             "merge_extra_floor_ms": by_v["merge"] / PEAK_HBM_GBS / 1e6,
         },
         "rope": rope,
+        "softmax_policies": policies,
         "vsa_k78": None if k78_ms is None else {
             "topk": k78,
             "ms_per_call": sum(k78_ms.values()),

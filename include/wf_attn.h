@@ -178,6 +178,52 @@ int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t
                           int32_t D, float scale, int32_t topk, float* o, float* lse,
                           float* o_coarse, void* stream);
 
+/* ------------------------------------------------------ softmax reference policies */
+
+/*
+ * "Anatomy of Wan2.2's 53.6x speedup", section "Fixed-max softmax is a
+ * numerical contract", weighs the online softmax's running row maximum (exact
+ * and stable, but every new maximum rescales the accumulated output) against
+ * a reduction constant taken once from the first selected tile (one pass, and
+ * the probabilities are unchanged by the shift, but a later, much larger score
+ * overflows the exponential).  The _ex entry points below take the policy:
+ *
+ *   WF_SOFTMAX_GUARDED          the library default (what wf_attn_dense and
+ *                               wf_vsa_fine use): the reference is an integer,
+ *                               set on the first tile and raised only when a
+ *                               tile's probabilities would exceed 2^16, which
+ *                               one vote per tile detects; exact and
+ *                               overflow-safe, one pass on the common path.
+ *   WF_SOFTMAX_RUNNING_MAX      the textbook online softmax: row maximum of
+ *                               every tile, output and row sum rescaled every
+ *                               tile.  Exact and safe; the comparison point.
+ *   WF_SOFTMAX_FIXED_FIRST_TILE the page's contract without a guard: the
+ *                               reference comes from the first tile and never
+ *                               moves.  Exact while every later score stays
+ *                               within about 88 (natural-log units) of the
+ *                               first tile's maximum; beyond that the row's
+ *                               output and lse become inf or NaN.  For
+ *                               measurement and for reproducing that failure,
+ *                               not for use.
+ */
+enum {
+  WF_SOFTMAX_GUARDED = 0,
+  WF_SOFTMAX_RUNNING_MAX = 1,
+  WF_SOFTMAX_FIXED_FIRST_TILE = 2
+};
+
+/* wf_attn_dense with a softmax policy (above); otherwise identical. */
+int32_t wf_attn_dense_ex(const void* q, const void* k, const void* v, float* o, float* lse,
+                         int32_t B, int32_t Hh, int32_t N, int32_t D, float scale,
+                         int32_t softmax_mode, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* wf_vsa_fine with a softmax policy (above); otherwise identical. */
+int32_t wf_vsa_fine_ex(const void* workspace, size_t workspace_bytes, const int32_t* idx,
+                       int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                       float scale, int32_t topk, int32_t softmax_mode, float* o, float* lse,
+                       void* stream);
+
 /* ------------------------------------------------------ 3D RoPE */
 
 /*

@@ -25,7 +25,7 @@ def wf():
 def test_every_declared_symbol_is_exported(wf):
     names = declared_functions()
     assert "wf_attn_dense" in names and "wf_vsa_coarse_topk" in names and "wf_vsa_fine" in names
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(wf.lib, n), f"{n} declared in wf_attn.h but not exported"
 
@@ -114,6 +114,13 @@ def test_vsa_argument_errors(wf):
     assert cr(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, -1.0, 32, FAKE, None, FAKE, 1 << 30, None) == 1
     assert cr(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 9, 1e4, 32, FAKE, None, FAKE, 1 << 30, None) == 1
     assert cr(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 1e4, 48, FAKE, None, FAKE, 1 << 30, None) == 1
+    dex = wf.lib.wf_attn_dense_ex
+    assert dex(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, 3, FAKE, 1 << 30, None) == 1
+    assert dex(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, -1, FAKE, 1 << 30, None) == 1
+    assert dex(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 96, 0.1, 1, FAKE, 1 << 30, None) == 2
+    fex = wf.lib.wf_vsa_fine_ex
+    assert fex(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 7, FAKE, None, None) == 1
+    assert fex(FAKE, 10, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 2, FAKE, None, None) == 3
     gated = wf.lib.wf_vsa_fine_gated
     assert gated(FAKE, 1 << 30, FAKE, None, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1
     assert gated(FAKE, 1 << 30, FAKE, FAKE + 4, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1

@@ -28,6 +28,8 @@ _SIGS = {
     "wf_abi_version": (_i32, []),
     "wf_attn_dense_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "wf_attn_dense": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "wf_attn_dense_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "wf_vsa_fine_ex": (_i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp]),
     "wf_vsa_num_cubes": (_i32, [_i32, _i32, _i32]),
     "wf_vsa_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "wf_vsa_coarse_topk": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
@@ -48,6 +50,8 @@ for _name, (_res, _args) in _SIGS.items():
     _fn.restype, _fn.argtypes = _res, _args
 
 WF_OK, WF_ERR_INVALID_ARG, WF_ERR_UNSUPPORTED, WF_ERR_WORKSPACE, WF_ERR_BAD_INDEX, WF_ERR_HIP = range(6)
+# softmax reference policies (wf_attn.h)
+WF_SOFTMAX_GUARDED, WF_SOFTMAX_RUNNING_MAX, WF_SOFTMAX_FIXED_FIRST_TILE = range(3)
 
 
 class WfError(RuntimeError):
@@ -108,8 +112,11 @@ def _workspace(nbytes: int, device, given=None):
 
 
 def wf_attn_dense(q, k, v, scale: Optional[float] = None, with_lse: bool = False,
-                  out=None, lse=None, workspace=None):
-    """Dense attention through wf_attn_dense.  Returns (o fp32 [B,Hh,N,D], lse or None)."""
+                  out=None, lse=None, workspace=None, softmax_mode: int = WF_SOFTMAX_GUARDED):
+    """Dense attention through wf_attn_dense (wf_attn_dense_ex for another softmax policy).
+
+    Returns (o fp32 [B,Hh,N,D], lse or None).
+    """
     torch = _torch()
     _qkv_check(q, k, v)
     B, Hh, N, D = q.shape
@@ -119,9 +126,14 @@ def wf_attn_dense(q, k, v, scale: Optional[float] = None, with_lse: bool = False
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
     ws = _workspace(dense_workspace_bytes(B, Hh, N, D), q.device, workspace)
-    _check(lib.wf_attn_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
-                             B, Hh, N, D, scale, ws.data_ptr(), ws.numel() * ws.element_size(),
-                             _stream_handle(q.device)), "wf_attn_dense")
+    if softmax_mode == WF_SOFTMAX_GUARDED:
+        _check(lib.wf_attn_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
+                                 B, Hh, N, D, scale, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream_handle(q.device)), "wf_attn_dense")
+    else:
+        _check(lib.wf_attn_dense_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
+                                    B, Hh, N, D, scale, int(softmax_mode), ws.data_ptr(),
+                                    ws.numel() * ws.element_size(), _stream_handle(q.device)), "wf_attn_dense_ex")
     return out, lse
 
 
@@ -183,8 +195,11 @@ def wf_vsa_coarse_topk(q, k, v, grid, topk: int, scale: Optional[float] = None,
 
 
 def wf_vsa_fine(workspace, idx, shape, grid, scale: Optional[float] = None, with_lse: bool = False,
-                out=None, lse=None):
-    """VSA fine stage through wf_vsa_fine.  shape = (B, Hh, N, D).  Returns (o, lse or None)."""
+                out=None, lse=None, softmax_mode: int = WF_SOFTMAX_GUARDED):
+    """VSA fine stage through wf_vsa_fine (wf_vsa_fine_ex for another softmax policy).
+
+    shape = (B, Hh, N, D).  Returns (o, lse or None).
+    """
     torch = _torch()
     B, Hh, N, D = shape
     T, H, W = grid
@@ -195,9 +210,14 @@ def wf_vsa_fine(workspace, idx, shape, grid, scale: Optional[float] = None, with
         out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=idx.device)
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=idx.device)
-    _check(lib.wf_vsa_fine(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                           idx.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3], out.data_ptr(),
-                           _ptr(lse), _stream_handle(idx.device)), "wf_vsa_fine")
+    if softmax_mode == WF_SOFTMAX_GUARDED:
+        _check(lib.wf_vsa_fine(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               idx.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3], out.data_ptr(),
+                               _ptr(lse), _stream_handle(idx.device)), "wf_vsa_fine")
+    else:
+        _check(lib.wf_vsa_fine_ex(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  idx.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3], int(softmax_mode),
+                                  out.data_ptr(), _ptr(lse), _stream_handle(idx.device)), "wf_vsa_fine_ex")
     return out, lse
 
 

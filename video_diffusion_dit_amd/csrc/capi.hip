@@ -131,9 +131,9 @@ size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D
   return wf::dense_workspace_bytes(B * Hh, N, D);
 }
 
-int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
-                      int32_t Hh, int32_t N, int32_t D, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+static int32_t dense(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
+                     int32_t Hh, int32_t N, int32_t D, float scale, int32_t softmax_mode,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   WF_CHECK_PTR(q);
   WF_CHECK_PTR(k);
   WF_CHECK_PTR(v);
@@ -149,10 +149,29 @@ int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, flo
     return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
                 need);
   WF_CHECK_PTR(workspace);
-  hipError_t e = wf::launch_dense(q, k, v, o, lse, B * Hh, N, D, scale, workspace,
+  hipError_t e = wf::launch_dense(q, k, v, o, lse, B * Hh, N, D, scale, softmax_mode, workspace,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "dense launch");
   return ok();
+}
+
+int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
+                      int32_t Hh, int32_t N, int32_t D, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return dense(q, k, v, o, lse, B, Hh, N, D, scale, WF_SOFTMAX_GUARDED, workspace, workspace_bytes,
+               stream);
+}
+
+static bool softmax_mode_ok(int32_t mode) {
+  return mode == WF_SOFTMAX_GUARDED || mode == WF_SOFTMAX_RUNNING_MAX || mode == WF_SOFTMAX_FIXED_FIRST_TILE;
+}
+
+int32_t wf_attn_dense_ex(const void* q, const void* k, const void* v, float* o, float* lse,
+                         int32_t B, int32_t Hh, int32_t N, int32_t D, float scale,
+                         int32_t softmax_mode, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!softmax_mode_ok(softmax_mode)) return fail(WF_ERR_INVALID_ARG, "softmax_mode %d", softmax_mode);
+  return dense(q, k, v, o, lse, B, Hh, N, D, scale, softmax_mode, workspace, workspace_bytes, stream);
 }
 
 int32_t wf_vsa_num_cubes(int32_t T, int32_t H, int32_t W) {
@@ -288,7 +307,23 @@ int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t
   if (int32_t st = vsa_fine_checks(workspace, workspace_bytes, idx, B, Hh, T, H, W, D, scale, topk,
                                    o, lse, s))
     return st;
-  hipError_t e = wf::launch_vsa_fine(workspace, idx, B * Hh, T, H, W, D, scale, topk, o, lse, s);
+  hipError_t e = wf::launch_vsa_fine(workspace, idx, B * Hh, T, H, W, D, scale, topk,
+                                     WF_SOFTMAX_GUARDED, o, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "VSA fine launch");
+  return ok();
+}
+
+int32_t wf_vsa_fine_ex(const void* workspace, size_t workspace_bytes, const int32_t* idx,
+                       int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                       float scale, int32_t topk, int32_t softmax_mode, float* o, float* lse,
+                       void* stream) {
+  if (!softmax_mode_ok(softmax_mode)) return fail(WF_ERR_INVALID_ARG, "softmax_mode %d", softmax_mode);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int32_t st = vsa_fine_checks(workspace, workspace_bytes, idx, B, Hh, T, H, W, D, scale, topk,
+                                   o, lse, s))
+    return st;
+  hipError_t e = wf::launch_vsa_fine(workspace, idx, B * Hh, T, H, W, D, scale, topk, softmax_mode,
+                                     o, lse, s);
   if (e != hipSuccess) return hip_fail(e, "VSA fine launch");
   return ok();
 }

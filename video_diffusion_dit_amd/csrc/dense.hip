@@ -54,8 +54,10 @@ __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict
 // into the slots K(t-1) and V(t-2) left, and waits for them at the end of its
 // next MFMA phase, so each copy has a phase to land.  Within an MFMA phase the
 // LDS operand reads run four MFMAs ahead of use; the first four are read at the
-// end of the wavefront's VALU phase, before the barrier.
-template <int D>
+// end of the wavefront's VALU phase, before the barrier.  SM selects the
+// softmax reference policy (softmax_tile; the library default is the guarded
+// integer reference).
+template <int D, int SM>
 __global__ void __launch_bounds__(512, 1)
 wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
              const uint16_t* __restrict__ vt, float* __restrict__ o, float* __restrict__ lse,
@@ -144,7 +146,7 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           if (t * 64 + key_row(1, r, half) >= N) s1[r] = -INFINITY;
         }
       }
-      softmax_tile<DB>(s0, s1, sl2, m, l, oacc, p2);
+      softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, p2);
     }
     mfma_prefill<D, 0>(ring, vnext, kcur, j, half);  // first operands of MFMA phase t+1: V(t) rows
     barrier_nofence();
@@ -174,7 +176,7 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
 template <int D>
 static hipError_t launch_dense_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* o,
-                                 float* lse, int BH, int N, float scale, uint16_t* vt,
+                                 float* lse, int BH, int N, float scale, int softmax_mode, uint16_t* vt,
                                  hipStream_t s) {
   const int Np = (N + 63) / 64 * 64;
   hipError_t e = wf_launch("wf_transpose_v", s, [&] {
@@ -184,10 +186,14 @@ static hipError_t launch_dense_d(const uint16_t* q, const uint16_t* k, const uin
   if (e != hipSuccess) return e;
   const int nqt = (N + 255) / 256;
   const long grid = (long)nqt * BH;
-  return wf_launch("wf_dense_fwd", s, [&] {
-    hipLaunchKernelGGL((wf_dense_fwd<D>), dim3((unsigned)grid), dim3(512), 0, s,
-                       q, k, vt, o, lse, N, Np, nqt, scale * kLog2e);
-  });
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(512), 0, s, q, k, vt, o, lse, N, Np, nqt, scale * kLog2e);
+  };
+  if (softmax_mode == kSoftmaxRunningMax)
+    return wf_launch("wf_dense_fwd_running_max", s, [&] { go(wf_dense_fwd<D, kSoftmaxRunningMax>); });
+  if (softmax_mode == kSoftmaxFixedFirst)
+    return wf_launch("wf_dense_fwd_fixed_first", s, [&] { go(wf_dense_fwd<D, kSoftmaxFixedFirst>); });
+  return wf_launch("wf_dense_fwd", s, [&] { go(wf_dense_fwd<D, kSoftmaxGuarded>); });
 }
 
 size_t dense_workspace_bytes(int BH, int N, int D) {
@@ -196,12 +202,12 @@ size_t dense_workspace_bytes(int BH, int N, int D) {
 }
 
 hipError_t launch_dense(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
-                        int N, int D, float scale, void* ws, hipStream_t s) {
+                        int N, int D, float scale, int softmax_mode, void* ws, hipStream_t s) {
   auto q16 = static_cast<const uint16_t*>(q), k16 = static_cast<const uint16_t*>(k),
        v16 = static_cast<const uint16_t*>(v);
   auto vt = static_cast<uint16_t*>(ws);
-  if (D == 128) return launch_dense_d<128>(q16, k16, v16, o, lse, BH, N, scale, vt, s);
-  return launch_dense_d<64>(q16, k16, v16, o, lse, BH, N, scale, vt, s);
+  if (D == 128) return launch_dense_d<128>(q16, k16, v16, o, lse, BH, N, scale, softmax_mode, vt, s);
+  return launch_dense_d<64>(q16, k16, v16, o, lse, BH, N, scale, softmax_mode, vt, s);
 }
 
 }  // namespace wf

@@ -7,11 +7,16 @@
 // top-k key cubes of every query cube, then run token-level attention of each
 // query cube over those cubes only.  Section "Roofline analysis set the 3.35
 // ms target" counts one output tile per (query cube, head).
+#include "wf_attn.h"
 #include "wf_device.hpp"
 #include "wf_launch.hpp"
 #include "wf_rope.hpp"
 
 namespace wf {
+
+static_assert(kSoftmaxGuarded == WF_SOFTMAX_GUARDED && kSoftmaxRunningMax == WF_SOFTMAX_RUNNING_MAX &&
+                  kSoftmaxFixedFirst == WF_SOFTMAX_FIXED_FIRST_TILE,
+              "softmax policy numbers of the C ABI and the kernels");
 
 // Cs: the cube count rounded up to a multiple of 32, the row stride of the
 // coarse scores and of the transposed cube means of V in the workspace.
@@ -433,8 +438,9 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
 // for only before the next P V, so it lands behind the next tile's scores and
 // softmax.  Padded key slots of edge cubes are masked; output rows are
 // scattered back to grid order, padded query slots are not written.  With
-// GATED the epilogue adds gate * Oc of the query cube (gated merge).
-template <int D, bool GATED>
+// GATED the epilogue adds gate * Oc of the query cube (gated merge).  SM
+// selects the softmax reference policy (softmax_tile).
+template <int D, bool GATED, int SM = kSoftmaxGuarded>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vct, const int* __restrict__ idx, float* __restrict__ o,
@@ -490,7 +496,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
         if (!((b >> 4) < lt && ((b >> 2) & 3) < lh && (b & 3) < lw)) s1[r] = -INFINITY;
       }
     }
-    softmax_tile<DB>(s0, s1, sl2, m, l, oacc, p2);
+    softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, p2);
     wait_tile_copies_keep<KP>();  // V(t) landed (it had the scores and the softmax to do so); K(t+1) may fly
     barrier_nofence();            // V(t) visible
     mfma_run<D, 0, NPV>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // O += P V(t)
@@ -611,17 +617,21 @@ hipError_t launch_vsa_check(const int* idx, int BH, int C, int topk, void* ws, s
 }
 
 hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H, int W, int D,
-                           float scale, int topk, float* o, float* lse, hipStream_t s) {
+                           float scale, int topk, int softmax_mode, float* o, float* lse, hipStream_t s) {
   const Grid3 g = make_grid(T, H, W);
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   const char* w = static_cast<const char*>(ws);
-  return wf_launch("wf_vsa_fine", s, [&] {
-    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, false>), dim3((unsigned)(BH * g.C)), dim3(128), 0, s,
-                       reinterpret_cast<const uint16_t*>(w + L.qc),
-                       reinterpret_cast<const uint16_t*>(w + L.kc),
-                       reinterpret_cast<const uint16_t*>(w + L.vct), idx, o, lse, nullptr, nullptr,
-                       g, topk, scale * kLog2e);
-  });
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(128), 0, s,
+                       reinterpret_cast<const uint16_t*>(w + L.qc), reinterpret_cast<const uint16_t*>(w + L.kc),
+                       reinterpret_cast<const uint16_t*>(w + L.vct), idx, o, lse, nullptr, nullptr, g, topk,
+                       scale * kLog2e);
+  };
+  if (softmax_mode == kSoftmaxRunningMax)
+    return wf_launch("wf_vsa_fine_running_max", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxRunningMax>); });
+  if (softmax_mode == kSoftmaxFixedFirst)
+    return wf_launch("wf_vsa_fine_fixed_first", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxFixedFirst>); });
+  return wf_launch("wf_vsa_fine", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded>); });
 }
 
 hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int BH, int T, int H,

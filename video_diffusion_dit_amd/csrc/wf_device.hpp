@@ -307,26 +307,53 @@ __device__ __forceinline__ float tile_probs(const f32x16& s0, const f32x16& s1, 
 // m, rescale O and l, and recompute the tile.  O / l is unchanged by the choice of reference, and the
 // references are integers, so the bf16 probabilities do not depend on when
 // the reference was raised (they differ by exact powers of two).
+//
+// Two other reference policies exist for comparison ("Fixed-max softmax is a
+// numerical contract" weighs them): SM = kSoftmaxRunningMax is the textbook
+// online softmax (row max of every tile, O and l rescaled every tile), and
+// SM = kSoftmaxFixedFirst takes the reference from the first tile and never
+// raises it -- one pass without the overflow check, exact until a later score
+// exceeds the first tile's maximum by about 88 (natural log units), where
+// exp overflows and the row's output becomes inf / NaN.
+constexpr int kSoftmaxGuarded = 0, kSoftmaxRunningMax = 1, kSoftmaxFixedFirst = 2;
+
+__device__ __forceinline__ float tile_row_max(const f32x16& s0, const f32x16& s1, float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+  return wave_max_pair(mx) * sl2;
+}
+
 template <int DB>
+__device__ __forceinline__ void rescale(f32x16* o, float& l, float alpha) {
+  l *= alpha;
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+}
+
+template <int DB, int SM = kSoftmaxGuarded>
 __device__ __forceinline__ void softmax_tile(const f32x16& s0, const f32x16& s1, float sl2, float& m, float& l,
                                              f32x16* o, bf16x2* p2) {
-  float lt = tile_probs(s0, s1, sl2, m, p2);
-  if (__ballot(!(lt <= 0x1p16f))) {  // first tile (m = -inf gives inf/NaN) or a big jump
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
-    mx = wave_max_pair(mx) * sl2;
-    const float mnew = fmaxf(m, ceilf(mx));  // integer references: a later raise rescales by a power of two
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+  if constexpr (SM == kSoftmaxRunningMax) {
+    const float mnew = fmaxf(m, tile_row_max(s0, s1, sl2));
+    rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));  // first tile: exp2(-inf) = 0 on zeros
     m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
-    lt = tile_probs(s0, s1, sl2, m, p2);
+    l += tile_probs(s0, s1, sl2, m, p2);
+  } else if constexpr (SM == kSoftmaxFixedFirst) {
+    if (m == -INFINITY) m = ceilf(tile_row_max(s0, s1, sl2));  // first tile only (every row at once)
+    l += tile_probs(s0, s1, sl2, m, p2);
+  } else {
+    float lt = tile_probs(s0, s1, sl2, m, p2);
+    if (__ballot(!(lt <= 0x1p16f))) {  // first tile (m = -inf gives inf/NaN) or a big jump
+      const float mnew = fmaxf(m, ceilf(tile_row_max(s0, s1, sl2)));  // integer: later raises rescale by 2^n
+      rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
+      m = mnew;
+      lt = tile_probs(s0, s1, sl2, m, p2);
+    }
+    l += lt;
   }
-  l += lt;
 }
 
 // Final normalisation and store of one wavefront's 32 x D output block: the

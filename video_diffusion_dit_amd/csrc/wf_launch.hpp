@@ -26,8 +26,9 @@ hipError_t launch_rope_qk(const void* q, const void* k, void* qo, void* ko, int 
 
 // Dense attention.
 size_t dense_workspace_bytes(int BH, int N, int D);
+// softmax_mode: 0 guarded integer reference, 1 running max, 2 fixed first-tile reference.
 hipError_t launch_dense(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
-                        int N, int D, float scale, void* ws, hipStream_t s);
+                        int N, int D, float scale, int softmax_mode, void* ws, hipStream_t s);
 
 // VSA workspace layout (byte offsets, each 256-byte aligned).
 struct VsaLayout {
@@ -43,7 +44,7 @@ hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH
 hipError_t launch_vsa_check(const int* idx, int BH, int C, int topk, void* ws, size_t flag_off,
                             hipStream_t s, int* bad);
 hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H, int W, int D,
-                           float scale, int topk, float* o, float* lse, hipStream_t s);
+                           float scale, int topk, int softmax_mode, float* o, float* lse, hipStream_t s);
 hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int BH, int T, int H,
                                  int W, int D, float scale, int topk, float* o, float* lse,
                                  float* o_coarse, hipStream_t s);
