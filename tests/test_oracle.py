@@ -34,6 +34,12 @@ Map of pins (function -> what fixes it):
   fp32 rounding steps of the fp64 rotation, and its bf16 rounding agrees
   with the fp64 mode's except on a sliver of near-ties (never by more than
   one bf16 step).
+* oracle.sta_plan / sta (sliding-tile attention, adopted definition): the
+  plan against its geometric definition cube by cube (window size, own cube
+  inside, centred where it fits, pushed inward at edges); the output against
+  a token-level brute force (an explicit allowed-key mask built from token
+  coordinates, softmax by math.exp); a window covering the whole cube grid
+  reduces to dense attention; a 1x1x1 window to attention within each cube.
 * oracle.round_bf16: matches the float32 round-to-nearest-even of synth on
   float32-representable values, resolves exact ties to even, and rounds fp64
   values just above a tie upward (where an fp32 intermediate would not).
@@ -593,3 +599,67 @@ def test_rope_fp32_mode():
     assert (np.abs(b64[differ] - b32[differ]) <= step * 1.0000001).all()
     with pytest.raises(ValueError):
         oracle.rope(x, T, H, W, precision="fp16")
+
+
+# --------------------------------------------------------------- sliding-tile attention
+
+def test_sta_plan_geometry():
+    T, H, W = 13, 10, 23                          # cube grid 4 x 3 x 6
+    plan = oracle.sta_plan(T, H, W, (3, 3, 3))
+    nt, nh, nw = 4, 3, 6
+    assert plan.shape == (72, 27)
+    for c in range(72):
+        ct, ch, cw = c // (nh * nw), (c // nw) % nh, c % nw
+        row = plan[c]
+        assert (np.diff(row) > 0).all() and c in row
+        coords = np.stack([row // (nh * nw), (row // nw) % nh, row % nw], 1)
+        for axis, (cc, n) in enumerate(((ct, nt), (ch, nh), (cw, nw))):
+            lo, hi = coords[:, axis].min(), coords[:, axis].max()
+            assert hi - lo == 2 and 0 <= lo and hi < n
+            if 1 <= cc <= n - 2:
+                assert lo == cc - 1                 # centred where it fits
+            else:
+                assert lo == (0 if cc == 0 else n - 3)   # pushed inward at the edges
+    assert oracle.window_start(0, 4, 10) == 0 and oracle.window_start(5, 4, 10) == 4
+    assert oracle.window_start(9, 4, 10) == 6
+    with pytest.raises(ValueError):
+        oracle.sta_plan(T, H, W, (5, 1, 1))
+
+
+def test_sta_token_brute_force():
+    T, H, W, D = 6, 5, 9, 8                       # cube grid 2 x 2 x 3, ragged on every axis
+    q, k, v = small_vsa_inputs(95, T, H, W, D)
+    tok = oracle.cube_layout(T, H, W)
+    s = 1 / math.sqrt(D)
+    window = (1, 2, 2)
+    o, lse = oracle.sta(q, k, v, tok, T, H, W, window, s)
+    nt, nh, nw = 2, 2, 3
+    N = T * H * W
+    for i in range(N):
+        ti, hi, wi = i // (H * W), (i // W) % H, i % W
+        ct, ch, cw = ti // 4, hi // 4, wi // 4
+        lo = [oracle.window_start(c, w, n) for c, w, n in ((ct, 1, nt), (ch, 2, nh), (cw, 2, nw))]
+        allowed = [j for j in range(N)
+                   if lo[0] <= j // (H * W) // 4 < lo[0] + 1 and lo[1] <= (j // W) % H // 4 < lo[1] + 2
+                   and lo[2] <= j % W // 4 < lo[2] + 2]
+        e = [math.exp(s * float(q[i] @ k[j])) for j in allowed]
+        tot = sum(e)
+        ref = sum(w_ * v[j] for w_, j in zip(e, allowed)) / tot
+        np.testing.assert_allclose(o[i], ref, atol=1e-12)
+        assert abs(lse[i] - math.log(tot)) < 1e-12
+
+
+def test_sta_closed_forms():
+    T, H, W, D = 7, 9, 6, 16                      # cube grid 2 x 3 x 2
+    q, k, v = small_vsa_inputs(96, T, H, W, D)
+    tok = oracle.cube_layout(T, H, W)
+    s = 1 / math.sqrt(D)
+    o, lse = oracle.sta(q, k, v, tok, T, H, W, (2, 3, 2), s)     # the whole cube grid
+    od, ld = oracle.attention(q, k, v, s)
+    np.testing.assert_allclose(o, od, atol=1e-12)
+    np.testing.assert_allclose(lse, ld, atol=1e-12)
+    o1, _ = oracle.sta(q, k, v, tok, T, H, W, (1, 1, 1), s)      # each cube on its own
+    for c in range(tok.shape[0]):
+        rows = tok[c][tok[c] >= 0]
+        ob, _ = oracle.attention(q[rows], k[rows], v[rows], s)
+        np.testing.assert_allclose(o1[rows], ob, atol=1e-12)
