@@ -234,6 +234,8 @@ def main():
         kern[name] = tot / n
     wf.profile_enable(False)
 
+    dense_tf_step = dense_flops(wd) / (kern["wf_dense_fwd"] * 1e-3) / 1e12  # for dense-equivalent times
+
     # extra record (not part of the step): VSA at the review's 78-of-624 operating point
     k78, k78_ms = synth.WORKLOADS["vsa_480p_k78"].topk, None
     if not args.no_extra:
@@ -340,6 +342,41 @@ def main():
                     "dense_fixed_first_over_guarded": pk["wf_dense_fwd_fixed_first"] / pk["wf_dense_fwd"],
                     "vsa_fine_running_max_over_guarded": pk["wf_vsa_fine_running_max"] / pk["wf_vsa_fine"],
                     "vsa_fine_fixed_first_over_guarded": pk["wf_vsa_fine_fixed_first"] / pk["wf_vsa_fine"]}
+
+    # extra record (not part of the step): sliding-tile attention on the two tuned grids, 40 heads,
+    # 5x5x5-cube windows (own inputs; the step's tensors are unchanged)
+    sta = None
+    if not args.no_extra:
+        sta = {}
+        for name in ("sta_36x48x48", "sta_18x48x80"):
+            ws_ = synth.WORKLOADS[name]
+            qs_, ks2, vs2 = (to_dev(x) for x in synth.make_qkv(ws_))
+            gs = (ws_.T, ws_.H, ws_.W)
+            os2 = torch.empty((ws_.B, ws_.Hh, ws_.N, ws_.D), dtype=torch.float32, device=dev)
+            wsb = torch.empty(wf.lib.wf_sta_workspace_bytes(ws_.B, ws_.Hh, *gs, ws_.D, *ws_.window),
+                              dtype=torch.uint8, device=dev)
+            wf.wf_sta(qs_, ks2, vs2, gs, ws_.window, out=os2, workspace=wsb)
+            torch.cuda.synchronize()
+            wf.profile_enable(True)
+            for _ in range(5):
+                wf.wf_sta(qs_, ks2, vs2, gs, ws_.window, out=os2, workspace=wsb)
+            torch.cuda.synchronize()
+            sk2 = {}
+            for kname in ("wf_vsa_gather", "wf_sta_plan", "wf_sta_fine"):
+                n, tot = wf.profile_query(kname)
+                sk2[kname] = tot / n
+            wf.profile_enable(False)
+            kk = ws_.window[0] * ws_.window[1] * ws_.window[2]
+            cubes = wf.num_cubes(*gs)
+            fine_fl = 4.0 * ws_.B * ws_.Hh * ws_.N * 64 * kk * ws_.D
+            ms = sum(sk2.values())
+            dense_ms = dense_flops(ws_) / (dense_tf_step * 1e12) * 1e3  # dense at this shape, at the step's rate
+            sta[name] = {"grid": list(gs), "heads": ws_.Hh, "cubes": cubes, "window": list(ws_.window),
+                         "key_cubes_per_query_cube": kk, "ms_per_call": ms, "kernel_ms": sk2,
+                         "fine_tflops": fine_fl / (sk2["wf_sta_fine"] * 1e-3) / 1e12,
+                         "dense_equivalent_ms_at_step_rate": dense_ms,
+                         "dense_equivalent_speedup": dense_ms / ms}
+            del qs_, ks2, vs2, os2, wsb
 
     # extra record (not part of the step): one GPU's share of the heads when 8 GPUs split them
     # (5 of 40 per CFG branch): the same kernels at Hh = 5 and full N
@@ -452,6 +489,7 @@ def main():
             "merge_extra_ms": gated_ms["wf_vsa_fine_gated"] - kern["wf_vsa_fine"],
             "merge_extra_floor_ms": by_v["merge"] / PEAK_HBM_GBS / 1e6,
         },
+        "sta": sta,
         "rope": rope,
         "softmax_policies": policies,
         "vsa_k78": None if k78_ms is None else {

@@ -178,6 +178,34 @@ int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t
                           int32_t D, float scale, int32_t topk, float* o, float* lse,
                           float* o_coarse, void* stream);
 
+/* ------------------------------------------------------ sliding-tile attention */
+
+/*
+ * Sliding-tile attention (STA).  "推理优化" (Inference optimization,
+ * WorldFoundry docs), approximate-attention section, entry "sta", lists
+ * weight-free sliding-tile attention for the Wan DiT on its tuned token grids
+ * (36, 48, 48) and (18, 48, 80), without tile or window sizes.  The library's
+ * definition, on VSA's cube layout (any grid VSA accepts):
+ *   - tiles are the 4x4x4 cubes of the padded grid (padded slots masked);
+ *   - query cube c attends to the cubes of a wt x wh x ww-cube window that on
+ *     each axis starts at clamp(c - (w-1)/2, 0, n - w): centred where it fits,
+ *     pushed inward at the grid's edge, so every cube sees wt*wh*ww cubes;
+ *   - each real query token attends to every real key token of those cubes:
+ *     o[i] = sum_j softmax_j(scale * q[i] . k[j]) v[j], lse as in wf_vsa_fine.
+ * This is wf_vsa_fine with a fixed plan instead of a top-k one.
+ *
+ *   q, k, v     bf16 [B][Hh][T*H*W][D]; D must be 128.
+ *   wt, wh, ww  window in cubes, 1 <= w <= ceil(axis/4).
+ *   o           fp32 [B][Hh][T*H*W][D], written; lse fp32 [B][Hh][T*H*W] or NULL.
+ *   plan        int32 [C][wt*wh*ww], written (ascending rows); may be NULL.
+ *   workspace   at least wf_sta_workspace_bytes() bytes.
+ */
+size_t wf_sta_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                              int32_t wt, int32_t wh, int32_t ww);
+int32_t wf_sta(const void* q, const void* k, const void* v, int32_t B, int32_t Hh, int32_t T, int32_t H,
+               int32_t W, int32_t D, float scale, int32_t wt, int32_t wh, int32_t ww, float* o, float* lse,
+               int32_t* plan, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------ softmax reference policies */
 
 /*

@@ -54,6 +54,7 @@ class Workload:
     structured: bool  # True: N(0,1) + 2*phi ; False: N(0,1) iid
     seed: int
     topk: Optional[int] = None
+    window: Optional[tuple] = None  # sliding-tile attention window, in cubes
     note: str = field(default="", compare=False)
 
     @property
@@ -84,6 +85,11 @@ WORKLOADS = {
     # the page's operating point: 78 of 624 cubes (87.5% sparsity)
     "vsa_480p_k78": Workload("vsa_480p_k78", 1, 40, 21, 30, 52, 128, True, 4, topk=78,
                              note="VSA, 480p grid, 624 cubes, top-78 (the review's 87.5% sparsity)"),
+    # sliding-tile attention on its two tuned token grids, 5x5x5-cube windows
+    "sta_36x48x48": Workload("sta_36x48x48", 1, 40, 36, 48, 48, 128, True, 6, window=(5, 5, 5),
+                             note="STA, grid 36x48x48 (1,296 cubes), window 5x5x5 cubes"),
+    "sta_18x48x80": Workload("sta_18x48x80", 1, 40, 18, 48, 80, 128, True, 7, window=(5, 5, 5),
+                             note="STA, grid 18x48x80 padded to 20x48x80 (1,200 cubes), window 5x5x5 cubes"),
 }
 
 
@@ -197,6 +203,7 @@ def make_qkv_heads(wl: Workload, heads: Iterable[tuple]) -> dict:
 
 
 def small_workload(name: str, B: int, Hh: int, T: int, H: int, W: int, D: int,
-                   structured: bool = True, seed: int = 11, topk: Optional[int] = None) -> Workload:
+                   structured: bool = True, seed: int = 11, topk: Optional[int] = None,
+                   window: Optional[tuple] = None) -> Workload:
     """An ad-hoc workload for tests (same recipe, any shape)."""
-    return Workload(name, B, Hh, T, H, W, D, structured, seed, topk)
+    return Workload(name, B, Hh, T, H, W, D, structured, seed, topk, window)

@@ -25,7 +25,7 @@ def wf():
 def test_every_declared_symbol_is_exported(wf):
     names = declared_functions()
     assert "wf_attn_dense" in names and "wf_vsa_coarse_topk" in names and "wf_vsa_fine" in names
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(wf.lib, n), f"{n} declared in wf_attn.h but not exported"
 
@@ -121,6 +121,14 @@ def test_vsa_argument_errors(wf):
     fex = wf.lib.wf_vsa_fine_ex
     assert fex(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 7, FAKE, None, None) == 1
     assert fex(FAKE, 10, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 2, FAKE, None, None) == 3
+    sta = wf.lib.wf_sta
+    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 0, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 64, 0.1, 1, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 2
+    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 2, 2, 2, FAKE, None, None, FAKE, 10, None) == 3
+    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 2, 2, 2, FAKE, None, FAKE + 2, FAKE, 1 << 30, None) == 1
+    assert wf.lib.wf_sta_workspace_bytes(1, 2, 5, 6, 7, 128, 3, 1, 1) == 0
+    assert wf.lib.wf_sta_workspace_bytes(1, 40, 36, 48, 48, 128, 5, 5, 5) > 0
     gated = wf.lib.wf_vsa_fine_gated
     assert gated(FAKE, 1 << 30, FAKE, None, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1
     assert gated(FAKE, 1 << 30, FAKE, FAKE + 4, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1

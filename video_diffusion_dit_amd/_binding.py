@@ -41,6 +41,9 @@ _SIGS = {
                           _vp]),
     "wf_vsa_coarse_topk_rope": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                        ctypes.c_double, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "wf_sta_workspace_bytes": (_sz, [_i32] * 9),
+    "wf_sta": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _vp,
+                      _vp, _sz, _vp]),
     "wf_profile_enable": (_i32, [_i32]),
     "wf_profile_query": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
                                 ctypes.POINTER(ctypes.c_double)]),
@@ -248,6 +251,33 @@ def wf_vsa_fine_gated(workspace, idx, gate, grid, scale: Optional[float] = None,
                                  out.data_ptr(), _ptr(lse), _ptr(o_coarse), _stream_handle(gate.device)),
            "wf_vsa_fine_gated")
     return out, lse, o_coarse
+
+
+def wf_sta(q, k, v, grid, window, scale: Optional[float] = None, with_lse: bool = False,
+           with_plan: bool = False, out=None, lse=None, workspace=None):
+    """Sliding-tile attention through wf_sta.  window = (wt, wh, ww) in cubes.
+
+    Returns (o, lse or None, plan int32 [C, wt*wh*ww] or None).
+    """
+    torch = _torch()
+    _qkv_check(q, k, v)
+    T, H, W = grid
+    wt, wh, ww = window
+    B, Hh, N, D = q.shape
+    if N != T * H * W:
+        raise ValueError(f"N = {N} but the grid has {T * H * W} tokens")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    plan = (torch.empty((num_cubes(T, H, W), wt * wh * ww), dtype=torch.int32, device=q.device)
+            if with_plan else None)
+    ws = _workspace(lib.wf_sta_workspace_bytes(B, Hh, T, H, W, D, wt, wh, ww), q.device, workspace)
+    _check(lib.wf_sta(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D, scale, wt, wh, ww,
+                      out.data_ptr(), _ptr(lse), _ptr(plan), ws.data_ptr(), ws.numel() * ws.element_size(),
+                      _stream_handle(q.device)), "wf_sta")
+    return out, lse, plan
 
 
 def vsa(q, k, v, grid, topk: int, scale: Optional[float] = None, with_lse: bool = False,

@@ -344,6 +344,44 @@ int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t
   return ok();
 }
 
+static int32_t sta_check(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D, int32_t wt,
+                         int32_t wh, int32_t ww) {
+  if (int32_t st = vsa_check_sizes(B, Hh, T, H, W, D)) return st;
+  const int nt = (T + 3) / 4, nh = (H + 3) / 4, nw = (W + 3) / 4;
+  if (wt < 1 || wt > nt || wh < 1 || wh > nh || ww < 1 || ww > nw)
+    return fail(WF_ERR_INVALID_ARG, "window %dx%dx%d cubes must fit the cube grid %dx%dx%d", wt, wh, ww, nt, nh,
+                nw);
+  return WF_OK;
+}
+
+size_t wf_sta_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
+                              int32_t wt, int32_t wh, int32_t ww) {
+  if (sta_check(B, Hh, T, H, W, D, wt, wh, ww) != WF_OK) return 0;
+  return wf::sta_layout(B * Hh, T, H, W, D, wt * wh * ww).total;
+}
+
+int32_t wf_sta(const void* q, const void* k, const void* v, int32_t B, int32_t Hh, int32_t T, int32_t H,
+               int32_t W, int32_t D, float scale, int32_t wt, int32_t wh, int32_t ww, float* o, float* lse,
+               int32_t* plan, void* workspace, size_t workspace_bytes, void* stream) {
+  WF_CHECK_PTR(q);
+  WF_CHECK_PTR(k);
+  WF_CHECK_PTR(v);
+  WF_CHECK_PTR(o);
+  WF_CHECK_OPT_PTR(lse);
+  WF_CHECK_OPT_PTR(plan);
+  if (int32_t st = sta_check(B, Hh, T, H, W, D, wt, wh, ww)) return st;
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
+  const size_t need = wf::sta_layout(B * Hh, T, H, W, D, wt * wh * ww).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0, need);
+  WF_CHECK_PTR(workspace);
+  hipError_t e = wf::launch_sta(q, k, v, B * Hh, T, H, W, D, scale, wt, wh, ww, o, lse, plan, workspace,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "STA launch");
+  return ok();
+}
+
 int32_t wf_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (on) {

@@ -445,7 +445,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vct, const int* __restrict__ idx, float* __restrict__ o,
     float* __restrict__ lse, const uint16_t* __restrict__ gate, const float* __restrict__ ocoarse,
-    Grid3 g, int k, float sl2) {
+    Grid3 g, int k, long plan_stride, float sl2) {
   constexpr int DB = D / 32, NPV = Pairs<D>::NPV, NQK = Pairs<D>::NQK;
   __shared__ __align__(16) char ks[Swz<D>::KB];
   __shared__ __align__(16) char vs[Swz<D>::VB];
@@ -454,7 +454,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / g.C, c = item % g.C;
   const long cube_base = (long)bh * g.C;
-  const int* plan = idx + ((long)bh * g.C + c) * k;
+  const int* plan = idx + bh * plan_stride + (long)c * k;  // plan_stride 0: one plan shared by all heads
   const int slot = wave * 32 + j;
 
   bf16x8 qop[D / 16];
@@ -515,6 +515,28 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
                           gate, GATED ? ocoarse + (cube_base + c) * D : nullptr);
   const int tok = slot_token(g, ct, ch, cw, slot);
   if (lse && tok >= 0 && half == 0) lse[head_row0 + tok] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+}
+
+// ---------------------------------------------------------------- sliding-tile plan
+// Sliding-tile attention ("推理优化", WorldFoundry docs, approximate attention,
+// entry "sta": weight-free, on tuned grids; tile and window sizes are not
+// given there): query cube c attends to the cubes of a (wt, wh, ww)-cube
+// window, on each axis starting at clamp(c - (w-1)/2, 0, n - w) -- centred
+// where it fits, pushed inward at the edges -- so every row has wt*wh*ww
+// cubes.  One thread per (cube, slot); slots run row-major over the window,
+// which lists the cubes in ascending order.
+__global__ void __launch_bounds__(256) wf_sta_plan(int* __restrict__ plan, Grid3 g, int wt, int wh, int ww) {
+  const int k = wt * wh * ww;
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long)g.C * k) return;
+  const int c = (int)(id / k), j = (int)(id % k);
+  int ct, ch, cw;
+  cube_coords(g, c, ct, ch, cw);
+  const int t0 = min(max(ct - (wt - 1) / 2, 0), g.nt - wt);
+  const int h0 = min(max(ch - (wh - 1) / 2, 0), g.nh - wh);
+  const int w0 = min(max(cw - (ww - 1) / 2, 0), g.nw - ww);
+  const int jt = j / (wh * ww), jh = (j / ww) % wh, jw = j % ww;
+  plan[id] = ((t0 + jt) * g.nh + (h0 + jh)) * g.nw + (w0 + jw);
 }
 
 // ---------------------------------------------------------------- plan check
@@ -625,13 +647,58 @@ hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H,
     hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(128), 0, s,
                        reinterpret_cast<const uint16_t*>(w + L.qc), reinterpret_cast<const uint16_t*>(w + L.kc),
                        reinterpret_cast<const uint16_t*>(w + L.vct), idx, o, lse, nullptr, nullptr, g, topk,
-                       scale * kLog2e);
+                       (long)g.C * topk, scale * kLog2e);
   };
   if (softmax_mode == kSoftmaxRunningMax)
     return wf_launch("wf_vsa_fine_running_max", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxRunningMax>); });
   if (softmax_mode == kSoftmaxFixedFirst)
     return wf_launch("wf_vsa_fine_fixed_first", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxFixedFirst>); });
   return wf_launch("wf_vsa_fine", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded>); });
+}
+
+// Sliding-tile attention workspace: the gather's regions, then the shared plan.
+StaLayout sta_layout(int BH, int T, int H, int W, int D, int k) {
+  const Grid3 g = make_grid(T, H, W);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  StaLayout L{};
+  const size_t tok = (size_t)BH * g.C * 64 * D * 2;
+  L.qc = 0;
+  L.kc = L.qc + up(tok);
+  L.vct = L.kc + up(tok);
+  L.qbar = L.vct + up(tok);
+  L.kbar = L.qbar + up((size_t)BH * g.C * D * 4);
+  L.vbt = L.kbar + up((size_t)BH * g.C * D * 4);
+  L.plan = L.vbt + up((size_t)2 * BH * D * g.Cs * 2);
+  L.total = L.plan + up((size_t)g.C * k * 4);
+  return L;
+}
+
+hipError_t launch_sta(const void* q, const void* k, const void* v, int BH, int T, int H, int W, int D,
+                      float scale, int wt, int wh, int ww, float* o, float* lse, int* plan_out, void* ws,
+                      hipStream_t s) {
+  const Grid3 g = make_grid(T, H, W);
+  const int kk = wt * wh * ww;
+  const StaLayout L = sta_layout(BH, T, H, W, D, kk);
+  char* w = static_cast<char*>(ws);
+  auto qc = reinterpret_cast<uint16_t*>(w + L.qc), kc = reinterpret_cast<uint16_t*>(w + L.kc),
+       vct = reinterpret_cast<uint16_t*>(w + L.vct);
+  int* plan = plan_out ? plan_out : reinterpret_cast<int*>(w + L.plan);
+  hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
+    hipLaunchKernelGGL((wf_vsa_gather<128, 0>), dim3((unsigned)(BH * g.C)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), qc, kc, vct, reinterpret_cast<float*>(w + L.qbar),
+                       reinterpret_cast<float*>(w + L.kbar), reinterpret_cast<uint16_t*>(w + L.vbt), g, 0.0);
+  });
+  if (e != hipSuccess) return e;
+  e = wf_launch("wf_sta_plan", s, [&] {
+    hipLaunchKernelGGL(wf_sta_plan, dim3((unsigned)(((long)g.C * kk + 255) / 256)), dim3(256), 0, s, plan, g,
+                       wt, wh, ww);
+  });
+  if (e != hipSuccess) return e;
+  return wf_launch("wf_sta_fine", s, [&] {
+    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, false, kSoftmaxGuarded>), dim3((unsigned)(BH * g.C)), dim3(128), 0, s,
+                       qc, kc, vct, plan, o, lse, nullptr, nullptr, g, kk, 0L, scale * kLog2e);
+  });
 }
 
 hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int BH, int T, int H,
@@ -654,7 +721,7 @@ hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int
                        reinterpret_cast<const uint16_t*>(w + L.qc),
                        reinterpret_cast<const uint16_t*>(w + L.kc),
                        reinterpret_cast<const uint16_t*>(w + L.vct), idx, o, lse,
-                       static_cast<const uint16_t*>(gate), oc, g, topk, scale * kLog2e);
+                       static_cast<const uint16_t*>(gate), oc, g, topk, (long)g.C * topk, scale * kLog2e);
   });
 }
 
