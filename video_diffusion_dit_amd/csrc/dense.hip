@@ -49,10 +49,11 @@ __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict
 // S(t) = K(t) Q^T) and a VALU phase (softmax of S(t)).  Half B runs one
 // barrier behind half A, so on every SIMD one wavefront is in its MFMA phase
 // (at raised issue priority) while the other is in its VALU phase.  K and V^T
-// tiles rotate through three LDS slots each: in its VALU phase t half A copies
-// K(t+2) and V(t+1) global -> LDS with buffer loads (no staging registers)
-// into the slots K(t-1) and V(t-2) left, and waits for them at the end of its
-// next MFMA phase, so each copy has a phase to land.  Within an MFMA phase the
+// tiles rotate through three LDS slots each, filled global -> LDS with buffer
+// loads (no staging registers): in its VALU phase t half A copies K(t+2) into
+// the slot K(t-1) left and half B copies V(t+2) into the slot V(t-1) left, so
+// the copy work is split evenly over the two halves; each waits for its copies
+// at the end of its next MFMA phase, so each copy has a phase to land.  Within an MFMA phase the
 // LDS operand reads run four MFMAs ahead of use; the first four are read at the
 // end of the wavefront's VALU phase, before the barrier.  SM selects the
 // softmax reference policy (softmax_tile; the library default is the guarded
@@ -99,45 +100,52 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // the first MFMA phase runs P V on zero probabilities: give it a zero V slot too
   for (int i = tid; i < Swz<D>::VB / 16; i += 512) reinterpret_cast<uint4*>(vt2)[i] = make_uint4(0, 0, 0, 0);
 
-  constexpr int KP = Swz<D>::KB / 1024 / 4, VP = Swz<D>::VB / 1024 / 4;  // copies per wavefront of half A
   const int nt = (N + 63) / 64;
   // Three K slots and three V slots: tile t's K sits in slot t % 3, its V in slot t % 3.
-  // Prologue: K(0), K(1) and V(0).
+  // Prologue: K(0), K(1) and V(0) by half A, V(1) by half B.
   const CopyOffsets<D, 4> coff(wq, lane, Np);
   const uint32_t vbytes = (uint32_t)D * Np * 2;  // one head's V^T
   if (!isB) {
     tile_copy<D, 4>(coff, kg, N, kt0, nullptr, 0, 0, nullptr, wq);
     tile_copy<D, 4>(coff, nt > 1 ? kg + 64 * D : nullptr, N - 64, kt1, vg, Np, vbytes, vt0, wq);
+  } else {
+    tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + 64, Np, nt > 1 ? vbytes - 128u : 0u, vt1, wq);
   }
-  __syncthreads();  // its fence waits for all three copies
+  __syncthreads();  // its fence waits for all four copies
   if (isB) __syncthreads();  // half B runs one phase behind
 
-  // one MFMA phase and one VALU phase for tile t; kcur = K(t), vprev = V(t-1).  In its VALU
-  // phase half A copies K(t+2) into knext and V(t+1) into vfill (the slots K(t-1) and V(t-2)
-  // left two barriers earlier) and waits only for the copies of the previous VALU phase,
-  // K(t+1) and V(t), which the next MFMA phase reads: each copy has two and a half phases
-  // to land.
+  // one MFMA phase and one VALU phase for tile t; kcur = K(t), vprev = V(t-1).  With half A's
+  // MFMA phase t in global phase 2t and its VALU phase t in 2t+1 (half B one phase later):
+  //   - half A copies K(t+2) into knext, the slot K(t-1) left, in its VALU phase (2t+1),
+  //     waits for it at the end of its MFMA phase t+1 (2t+2) and so publishes it from 2t+3;
+  //     K(t+2) is first read in 2t+4;
+  //   - half B copies V(t+2) into vprev's slot, V(t-1), which both halves finished reading in
+  //     their MFMA phases t, in its VALU phase (2t+2), waits at the end of its MFMA phase t+1
+  //     (2t+3) and publishes it from 2t+4; V(t+2) is first read by half A's operand prefetch
+  //     at the end of 2t+5.
+  // So each copy has one full phase to land, and both halves issue 4 copies per VALU phase.
   // The first operands of every MFMA phase are read at the end of the wavefront's previous
   // VALU phase, before the barrier, so the matrix pipe does not idle through the LDS latency
-  // at each phase start.  Those operands are V(t-1) rows, so V(t-1) must be in LDS one phase
-  // before its MFMA phase: half A waits for the copies of its VALU phase t at the end of its
-  // MFMA phase t+1 (one phase of latency), which publishes K(t+2) and V(t+1) from phase 2t+3
-  // on; both are first read in phase 2t+4 (V(t+1) by the prefetch at the end of 2t+3).
+  // at each phase start.
   uint4 ring[kRing];
-  auto phase_pair = [&](auto copier_c, int t, const char* kcur, const char* vprev, char* knext, char* vfill,
+  auto phase_pair = [&](auto half_a_c, int t, const char* kcur, const char* vprev, char* knext,
                         const char* vnext) __attribute__((always_inline)) {
-    constexpr bool COPIER = decltype(copier_c)::value;
+    constexpr bool HALF_A = decltype(half_a_c)::value;  // half A copies K tiles, half B V^T tiles
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);  // MFMA phase first at the SIMD's issue arbiter
     mfma_run<D, 0, Pairs<D>::NPV + Pairs<D>::NQK, true>(vprev, kcur, p2, qop, oacc, s0, s1, j, half, ring);
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (COPIER) wait_tile_copies();  // K(t+1), V(t) landed
+    wait_tile_copies();  // half A: K(t+1) landed; half B: V(t+1) landed
     barrier_nofence();
-    // Always 8 copy instructions: a tile past the end gets a zero-length descriptor (no
-    // memory access) into a slot nobody reads again.
-    if constexpr (COPIER)
-      tile_copy<D, 4>(coff, kg + (long)(t + 2) * 64 * D, N - (t + 2) * 64, knext, vg + (long)(t + 1) * 64, Np,
-                      t + 1 < nt ? vbytes - (uint32_t)(t + 1) * 128 : 0u, vfill, wq);
+    // Always 4 copy instructions per wavefront: a tile past the end gets a zero-length
+    // descriptor (no memory access) into a slot nobody reads again.  Half A copies K(t+2) into
+    // K(t-1)'s slot; half B, one phase later, copies V(t+2) into V(t-1)'s slot, which both
+    // halves finished reading in their MFMA phases t.
+    if constexpr (HALF_A)
+      tile_copy<D, 4>(coff, kg + (long)(t + 2) * 64 * D, N - (t + 2) * 64, knext, nullptr, 0, 0u, nullptr, wq);
+    else
+      tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + (long)(t + 2) * 64, Np,
+                      t + 2 < nt ? vbytes - (uint32_t)(t + 2) * 128 : 0u, const_cast<char*>(vprev), wq);
     if (t < nt) {
       if ((t + 1) * 64 > N) {  // ragged last tile: keys >= N do not exist
 #pragma unroll
@@ -152,23 +160,21 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     barrier_nofence();
   };
   // unrolled by three so every LDS array is named statically, and instantiated once per half
-  // (copier or not) so the compiler tracks the copies on straight-line paths
-  auto tile_loop = [&](auto copier_c) __attribute__((always_inline)) {
+  // (half A or B) so the compiler tracks the copies on straight-line paths
+  auto tile_loop = [&](auto half_a_c) __attribute__((always_inline)) {
     mfma_prefill<D, 0>(ring, vt2, kt0, j, half);  // MFMA phase 0: V(-1), the zero slot
     for (int t = 0; t <= nt; t += 3) {
-      phase_pair(copier_c, t, kt0, vt2, kt2, vt1, vt0);
+      phase_pair(half_a_c, t, kt0, vt2, kt2, vt0);
       if (t + 1 <= nt) {  // nested, so every path into a phase passes the previous phase's wait
-        phase_pair(copier_c, t + 1, kt1, vt0, kt0, vt2, vt1);
-        if (t + 2 <= nt) phase_pair(copier_c, t + 2, kt2, vt1, kt1, vt0, vt2);
+        phase_pair(half_a_c, t + 1, kt1, vt0, kt0, vt1);
+        if (t + 2 <= nt) phase_pair(half_a_c, t + 2, kt2, vt1, kt1, vt2);
       }
     }
   };
   if (!isB) tile_loop(std::true_type());
   else tile_loop(std::false_type());
-  if (!isB) {
-    wait_tile_copies();  // no copy may still be writing LDS when the workgroup ends
-    barrier_nofence();   // same barrier count in both halves
-  }
+  wait_tile_copies();          // no copy may still be writing LDS when the workgroup ends
+  if (!isB) barrier_nofence();  // same barrier count in both halves
 
   const float lse_row = finish_store<DB>(oacc, m, l, qrow < N ? o + (base + qrow) * D : nullptr, half);
   if (lse && qrow < N && half == 0) lse[base + qrow] = lse_row;
