@@ -144,3 +144,29 @@ def test_profile_query_without_records(wf):
     n, ms = ctypes.c_int64(), ctypes.c_double()
     assert wf.lib.wf_profile_query(b"wf_dense_fwd", ctypes.byref(n), ctypes.byref(ms)) == 1
     assert wf.lib.wf_profile_enable(0) == 0
+
+
+def test_error_detail_is_per_thread(wf):
+    """wf_last_error_detail is thread-local: concurrent failures each read back their own message."""
+    import threading
+    results = {}
+    barrier = threading.Barrier(8)
+
+    def worker(i):
+        barrier.wait()
+        for _ in range(200):
+            topk = 9 + i                       # 5x6x7 has 8 cubes: every topk here is rejected
+            st = wf.lib.wf_vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 5, 6, 7, 128, 0.1, topk, FAKE, None, FAKE,
+                                           1 << 30, None)
+            msg = wf.lib.wf_last_error_detail()
+            if st != 1 or f"topk {topk} ".encode() not in msg:
+                results[i] = msg
+                return
+        results[i] = b"ok"
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert all(v == b"ok" for v in results.values()) and len(results) == 8, results

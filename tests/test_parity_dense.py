@@ -170,3 +170,23 @@ def test_dense_long_ragged_sampled(wf):
     assert_close(o[0, 0][rows], ref_o, f"O ({rows.size} rows)")
     assert errors(lse[0, 0][rows], ref_l)[0] <= LSE_MAX_ABS
     assert np.isfinite(o).all()
+
+
+def test_dense_concurrent_streams(wf):
+    """Calls are reentrant: two streams, each with its own workspace, running at once give the
+    same bits as the calls made one after the other."""
+    import torch
+    wl = synth.small_workload("dense_streams", 1, 6, 9, 11, 13, 128, structured=True, seed=120)
+    log("dense on two concurrent streams, 6 heads x 1287 tokens")
+    q, k, v = synth.make_qkv(wl)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    ref, _ = wf.wf_attn_dense(qd, kd, vd)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for st in (s1, s2):
+        with torch.cuda.stream(st):
+            outs.append(wf.wf_attn_dense(qd, kd, vd)[0])
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
