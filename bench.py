@@ -378,6 +378,48 @@ def main():
                          "dense_equivalent_speedup": dense_ms / ms}
             del qs_, ks2, vs2, os2, wsb
 
+    # extra record (not part of the step): the 720p shape -- dense attention on the CFG pair at
+    # 21x45x80 = 75,600 tokens and VSA top-64 of 1,440 cubes on the same tensors
+    r720 = None
+    if not args.no_extra:
+        wd7, wv7 = synth.WORKLOADS["dense_720p_cfg"], synth.WORKLOADS["vsa_720p"]
+        q7, k7, v7 = (to_dev(x) for x in synth.make_qkv(wv7))
+        g7 = (wv7.T, wv7.H, wv7.W)
+        C7 = wf.num_cubes(*g7)
+        o7 = torch.empty((wv7.B, wv7.Hh, wv7.N, wv7.D), dtype=torch.float32, device=dev)
+        wsd7 = torch.empty(wf.dense_workspace_bytes(wd7.B, wd7.Hh, wd7.N, wd7.D), dtype=torch.uint8, device=dev)
+        wsv7 = torch.empty(wf.vsa_workspace_bytes(wv7.B, wv7.Hh, *g7, wv7.D), dtype=torch.uint8, device=dev)
+        idx7 = torch.empty((wv7.B, wv7.Hh, C7, wv7.topk), dtype=torch.int32, device=dev)
+
+        def run720():
+            wf.wf_attn_dense(q7, k7, v7, out=o7, workspace=wsd7)
+            wf.wf_vsa_coarse_topk(q7, k7, v7, g7, wv7.topk, idx=idx7, workspace=wsv7)
+            wf.wf_vsa_fine(wsv7, idx7, (wv7.B, wv7.Hh, wv7.N, wv7.D), g7, out=o7)
+
+        run720()
+        torch.cuda.synchronize()
+        wf.profile_enable(True)
+        for _ in range(3):
+            run720()
+        torch.cuda.synchronize()
+        k7ms = {}
+        for name in ("wf_transpose_v", "wf_dense_fwd", "wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine"):
+            n, tot = wf.profile_query(name)
+            k7ms[name] = tot / n
+        wf.profile_enable(False)
+        d7 = k7ms["wf_transpose_v"] + k7ms["wf_dense_fwd"]
+        v7ms = k7ms["wf_vsa_gather"] + k7ms["wf_vsa_scores"] + k7ms["wf_vsa_topk"] + k7ms["wf_vsa_fine"]
+        f7 = vsa_flops(wv7, C7)
+        r720 = {"grid": list(g7), "B": wv7.B, "heads": wv7.Hh, "tokens": wv7.N, "cubes": C7, "topk": wv7.topk,
+                "dense_ms_per_call": d7,
+                "dense_tflops_kernel": dense_flops(wd7) / (k7ms["wf_dense_fwd"] * 1e-3) / 1e12,
+                "dense_frac_bf16_peak": dense_flops(wd7) / (k7ms["wf_dense_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "vsa_ms_per_call": v7ms,
+                "vsa_fine_tflops": f7["fine"] / (k7ms["wf_vsa_fine"] * 1e-3) / 1e12,
+                "dense_equivalent_speedup": d7 / v7ms, "ideal_speedup": C7 / wv7.topk,
+                "kernel_ms": k7ms}
+        del q7, k7, v7, o7, wsd7, wsv7, idx7
+
     # extra record (not part of the step): one GPU's share of the heads when 8 GPUs split them
     # (5 of 40 per CFG branch): the same kernels at Hh = 5 and full N
     share = None
@@ -489,6 +531,7 @@ def main():
             "merge_extra_ms": gated_ms["wf_vsa_fine_gated"] - kern["wf_vsa_fine"],
             "merge_extra_floor_ms": by_v["merge"] / PEAK_HBM_GBS / 1e6,
         },
+        "shape_720p": r720,
         "sta": sta,
         "rope": rope,
         "softmax_policies": policies,
