@@ -611,13 +611,24 @@ hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH
   if (e != hipSuccess) return e;
   const long rows = (long)BH * g.C;
   const dim3 grid((unsigned)((rows + 3) / 4));
+  // E candidates per lane: the smallest instantiated E with 64 * E >= C (the bitwise search costs
+  // E ballots per bit, so padding E wastes work)
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, sc, idx, stat, rows, g.C, g.Cs, topk);
+  };
   return wf_launch("wf_vsa_topk", s, [&] {
-    if (g.C <= 1024)
-      hipLaunchKernelGGL(wf_vsa_topk<16>, grid, dim3(256), 0, s, sc, idx, stat, rows, g.C, g.Cs, topk);
-    else if (g.C <= 2048)
-      hipLaunchKernelGGL(wf_vsa_topk<32>, grid, dim3(256), 0, s, sc, idx, stat, rows, g.C, g.Cs, topk);
-    else
-      hipLaunchKernelGGL(wf_vsa_topk<64>, grid, dim3(256), 0, s, sc, idx, stat, rows, g.C, g.Cs, topk);
+    const int e = (g.C + 63) / 64;
+    if (e <= 2) go(wf_vsa_topk<2>);
+    else if (e <= 4) go(wf_vsa_topk<4>);
+    else if (e <= 8) go(wf_vsa_topk<8>);
+    else if (e <= 10) go(wf_vsa_topk<10>);
+    else if (e <= 12) go(wf_vsa_topk<12>);
+    else if (e <= 16) go(wf_vsa_topk<16>);
+    else if (e <= 20) go(wf_vsa_topk<20>);
+    else if (e <= 24) go(wf_vsa_topk<24>);
+    else if (e <= 32) go(wf_vsa_topk<32>);
+    else if (e <= 48) go(wf_vsa_topk<48>);
+    else go(wf_vsa_topk<64>);
   });
 }
 
