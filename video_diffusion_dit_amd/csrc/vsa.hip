@@ -167,57 +167,75 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
 }
 
 // ---------------------------------------------------------------- coarse scores
-// S[bh][c][c'] = scale * sum_d Qbar[c][d] Kbar[c'][d] in fp32; 64x64 output
-// tile per workgroup, 4x4 per thread.  s has row stride Cs and -inf in columns
-// C..Cs-1; s_user (optional) gets the same scores with row stride C.
+// S[bh][c][c'] = scale * sum_d Qbar[c][d] Kbar[c'][d] in fp32 on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32).  One workgroup (4 wavefronts) per 128x128
+// tile of S, a 64x64 tile (2x2 blocks of 32x32) per wavefront, so each operand
+// row a wavefront loads feeds two blocks.  The sum over d is order-free, so
+// lane half h takes d = 32u + 16h + s at step s of chunk u for both operands:
+// each lane's operands are 16 consecutive floats of one row, read straight
+// from memory (L2) as four 16-byte loads, no LDS.  s has row stride Cs and -inf in
+// columns C..Cs-1; s_user (optional) gets the same scores with row stride C.
 template <int D>
 __global__ void __launch_bounds__(256) wf_vsa_scores(const float* __restrict__ qbar,
                                                      const float* __restrict__ kbar,
                                                      float* __restrict__ s, float* __restrict__ s_user,
-                                                     int C, int Cs, int ntile, float scale) {
-  constexpr int DK = 32;
-  __shared__ float As[DK][64 + 4];
-  __shared__ float Bs[DK][64 + 4];
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-  const int per_head = ntile * ntile;
+                                                     int C, int Cs, int ntr, int ntc, float scale) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, j = lane % 32,
+            h = lane / 32;
+  const int per_head = ntr * ntc;
   const int bh = blockIdx.x / per_head, rem = blockIdx.x % per_head;
-  const int r0 = (rem / ntile) * 64, c0 = (rem % ntile) * 64;
-  const float* A = qbar + (long)bh * C * D;
-  const float* Bm = kbar + (long)bh * C * D;
-  float acc[4][4] = {};
-  for (int d0 = 0; d0 < D; d0 += DK) {
-    for (int id = tid; id < 64 * DK; id += 256) {
-      const int r = id / DK, dd = id % DK;
-      As[dd][r] = (r0 + r < C) ? A[(long)(r0 + r) * D + d0 + dd] : 0.f;
-      Bs[dd][r] = (c0 + r < C) ? Bm[(long)(c0 + r) * D + d0 + dd] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int dd = 0; dd < DK; ++dd) {
-      float a[4], b[4];
+  // workgroup tile 128 x 128, wavefront tile 64 x 64 = 2 x 2 blocks of 32 x 32
+  const int r0 = (rem / ntc) * 128 + (wave >> 1) * 64, c0 = (rem % ntc) * 128 + (wave & 1) * 64;
+  const float* arow[2];
+  const float* brow[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = As[dd][ty * 4 + i]; b[i] = Bs[dd][tx * 4 + i]; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = __builtin_fmaf(a[i], b[jj], acc[i][jj]);
-    }
-    __syncthreads();
+  for (int x = 0; x < 2; ++x) {
+    arow[x] = qbar + ((long)bh * C + min(r0 + 32 * x + j, C - 1)) * D + h * 16;
+    brow[x] = kbar + ((long)bh * C + min(c0 + 32 * x + j, C - 1)) * D + h * 16;
   }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.f;
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    f32x4 a[2][4], bq[2][4];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        a[x][v] = *reinterpret_cast<const f32x4*>(arow[x] + u * 32 + v * 4);
+        bq[x][v] = *reinterpret_cast<const f32x4*>(brow[x] + u * 32 + v * 4);
+      }
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x][st / 4][st % 4], bq[y][st / 4][st % 4], acc[x][y], 0, 0, 0);
+  }
+  // block (x, y): lane (j, h) holds S[r0 + 32x + 8*(i/4) + 4h + i%4][c0 + 32y + j]
   float* out = s + (long)bh * C * Cs;
   float* user = s_user ? s_user + (long)bh * C * C : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + ty * 4 + i;
-    if (r >= C) continue;
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int cc = c0 + tx * 4 + jj;
-      const float x = acc[i][jj] * scale;
-      if (cc < Cs) out[(long)r * Cs + cc] = cc < C ? x : -INFINITY;
-      if (user && cc < C) user[(long)r * C + cc] = x;
+    for (int y = 0; y < 2; ++y) {
+      const int cc = c0 + 32 * y + j;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = r0 + 32 * x + 8 * (i / 4) + 4 * h + i % 4;
+        if (r >= C) continue;
+        const float val = acc[x][y][i] * scale;
+        if (cc < Cs) out[(long)r * Cs + cc] = cc < C ? val : -INFINITY;
+        if (user && cc < C) user[(long)r * C + cc] = val;
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------- top-k
@@ -603,10 +621,10 @@ hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH
   else
     e = wf_launch("wf_vsa_gather", s, [&] { gather(wf_vsa_gather<128, 0>); });
   if (e != hipSuccess) return e;
-  const int nt = (g.C + 63) / 64;
+  const int ntr = (g.C + 127) / 128, ntc = (g.Cs + 127) / 128;
   e = wf_launch("wf_vsa_scores", s, [&] {
-    hipLaunchKernelGGL(wf_vsa_scores<128>, dim3((unsigned)(BH * nt * nt)), dim3(256), 0, s, qbar,
-                       kbar, sc, scores_out, g.C, g.Cs, nt, scale);
+    hipLaunchKernelGGL(wf_vsa_scores<128>, dim3((unsigned)((long)BH * ntr * ntc)), dim3(256), 0, s, qbar,
+                       kbar, sc, scores_out, g.C, g.Cs, ntr, ntc, scale);
   });
   if (e != hipSuccess) return e;
   const long rows = (long)BH * g.C;
