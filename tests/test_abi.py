@@ -86,6 +86,18 @@ def coarse(wf, **kw):
                                      a["wsb"], None)
 
 
+def test_launch_grid_limits(wf):
+    """Shapes whose launch grids would not fit in 31 bits are refused up front, whatever workspace
+    size the caller declares."""
+    big = (1 << 62)
+    # dense: B * Hh * ceil(N / 64) workgroups for the V^T transpose
+    assert wf.lib.wf_attn_dense(FAKE, FAKE, FAKE, FAKE, None, 1, 1 << 23, 1 << 20, 128, 0.1, FAKE, big, None) == 2
+    assert b"too many workgroups" in wf.lib.wf_last_error_detail()
+    # VSA: B * Hh * C workgroups (C = 4096 here)
+    assert coarse(wf, B=1, Hh=1 << 20, T=61, H=62, W=63, wsb=big) == 2
+    assert b"too many workgroups" in wf.lib.wf_last_error_detail()
+
+
 def test_vsa_argument_errors(wf):
     assert coarse(wf, idx=None) == 1
     assert coarse(wf, topk=0) == 1

@@ -142,6 +142,8 @@ static int32_t dense(const void* q, const void* k, const void* v, float* o, floa
   if (!sizes_ok(B, Hh, N, D))
     return fail(WF_ERR_INVALID_ARG, "bad sizes B=%d Hh=%d N=%d D=%d", B, Hh, N, D);
   if (D != 64 && D != 128) return fail(WF_ERR_UNSUPPORTED, "head dimension %d (64 or 128)", D);
+  if ((long long)B * Hh * ((N + 63) / 64) >= (1ll << 31))  // the V^T transpose's grid, the largest
+    return fail(WF_ERR_UNSUPPORTED, "B=%d Hh=%d N=%d: too many workgroups for one launch", B, Hh, N);
   if (!isfinite(scale) || !(scale > 0.f))
     return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
   const size_t need = wf::dense_workspace_bytes(B * Hh, N, D);
@@ -190,6 +192,8 @@ static int32_t vsa_check_sizes(int32_t B, int32_t Hh, int32_t T, int32_t H, int3
     return fail(WF_ERR_INVALID_ARG, "bad sizes B=%d Hh=%d padded tokens=%lld D=%d", B, Hh, Np, D);
   if (D != 128) return fail(WF_ERR_UNSUPPORTED, "VSA head dimension %d (only 128)", D);
   if (C > 4096) return fail(WF_ERR_UNSUPPORTED, "%d cubes (at most 4096)", C);
+  if ((long long)B * Hh * C >= (1ll << 31))  // one workgroup per (head, cube) in the gather and fine stage
+    return fail(WF_ERR_UNSUPPORTED, "B=%d Hh=%d with %d cubes: too many workgroups for one launch", B, Hh, C);
   if ((long long)C * C >= (1ll << 31))
     return fail(WF_ERR_UNSUPPORTED, "%d cubes: score matrix too large", C);
   return WF_OK;

@@ -1,4 +1,4 @@
-// Internal host-side interface between the C ABI (capi.cpp) and the kernels.
+// Internal host-side interface between the C ABI (capi.hip) and the kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -6,7 +6,7 @@
 
 namespace wf {
 
-// Per-kernel timing hooks (capi.cpp): when timing is enabled, a HIP event is
+// Per-kernel timing hooks (capi.hip): when timing is enabled, a HIP event is
 // recorded on the launch stream before and after the launch.
 int prof_begin(const char* name, hipStream_t s);
 void prof_end(int slot, hipStream_t s);
