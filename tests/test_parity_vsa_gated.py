@@ -144,3 +144,49 @@ def test_vsa_gated_error_paths(wf):
         wf.wf_vsa_fine_gated(ws[:64], idx, qd, (5, 6, 7))
     assert e.value.status == 3
     torch.cuda.synchronize()
+
+
+def test_vsa_gated_after_fused_rope(wf):
+    """The gated call on the workspace of the RoPE-fused coarse stage equals the oracle's gated merge on
+    the oracle-rotated Q and K (the whole VSA chain with both additions)."""
+    import torch
+    wl = synth.small_workload("vsa_gated_rope", 1, 2, 9, 10, 11, 128, structured=True, seed=513, topk=4)
+    log("vsa gated after fused rope, grid 9x10x11")
+    q, k, v = synth.make_qkv(wl)
+    gate = synth.make_gate(wl)
+    grid = (wl.T, wl.H, wl.W)
+    idx, _, ws = wf.wf_vsa_coarse_topk(to_device(q), to_device(k), to_device(v), grid, wl.topk,
+                                       rope_theta=10000.0, rope_precision=64)
+    o, lse, oc = wf.wf_vsa_fine_gated(ws, idx, to_device(gate), grid, with_lse=True, with_coarse=True)
+    torch.cuda.synchronize()
+    g = dict(idx=idx.cpu().numpy(), o=o.cpu().numpy(), lse=lse.cpu().numpy(), oc=oc.cpu().numpy())
+    tok = oracle.cube_layout(wl.T, wl.H, wl.W)
+    rot = lambda x: synth.bf16_bits(np.stack([np.stack([
+        oracle.rope_bf16(synth.bits_to_f64(x[b, h]), wl.T, wl.H, wl.W, 10000.0, "fp64").astype(np.float32)
+        for h in range(wl.Hh)]) for b in range(wl.B)]))
+    qr, kr = rot(q), rot(k)
+    for h in range(wl.Hh):
+        qf, kf, vf = synth.bits_to_f64(qr[0, h]), synth.bits_to_f64(kr[0, h]), synth.bits_to_f64(v[0, h])
+        oc_ref = oracle.coarse_output(oracle.pool(qf, tok), oracle.pool(kf, tok), oracle.pool(vf, tok), wl.scale)
+        assert_close(g["oc"][0, h], oc_ref, f"O_coarse after rope h{h}", COARSE_MAX_ABS, COARSE_MEAN_ABS)
+        o_ref, l_ref = oracle.gated(qf, kf, vf, tok, g["idx"][0, h], wl.scale, synth.bits_to_f64(gate[0, h]))
+        assert_close(g["o"][0, h], o_ref, f"gated O after rope h{h}")
+        assert errors(g["lse"][0, h], l_ref)[0] <= LSE_MAX_ABS
+
+
+def test_vsa_gated_validates_plans(wf, monkeypatch):
+    import torch
+    wl = synth.small_workload("vsa_gated_val", 1, 1, 9, 10, 11, 128, structured=True, seed=514, topk=3)
+    log("vsa gated with WF_VALIDATE, bad plan")
+    q, k, v = synth.make_qkv(wl)
+    grid = (wl.T, wl.H, wl.W)
+    idx, _, ws = wf.wf_vsa_coarse_topk(to_device(q), to_device(k), to_device(v), grid, wl.topk)
+    bad = idx.clone()
+    bad[0, 0, 4, 2] = bad[0, 0, 4, 1]          # a repeated cube: not strictly ascending
+    monkeypatch.setenv("WF_VALIDATE", "1")
+    wf.wf_vsa_fine_gated(ws, idx, to_device(q), grid)   # the coarse stage's own plan passes
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_vsa_fine_gated(ws, bad, to_device(q), grid)
+    assert e.value.status == 4
+    monkeypatch.delenv("WF_VALIDATE")
+    torch.cuda.synchronize()
