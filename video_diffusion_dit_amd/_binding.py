@@ -86,6 +86,23 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _expect(t, name: str, shape, dtype, device) -> None:
+    """The library sees raw pointers only: every tensor handed to it is checked here for device,
+    dtype, layout and exact shape, so a wrong tensor raises instead of being read out of bounds."""
+    if t is None:
+        return
+    if (not t.is_cuda or t.device != device or t.dtype != dtype or not t.is_contiguous()
+            or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}; "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         + ("" if t.is_contiguous() else " (not contiguous)"))
+
+
+def _expect_workspace(ws, device) -> None:
+    if not ws.is_cuda or ws.device != device or not ws.is_contiguous() or ws.dim() != 1:
+        raise ValueError(f"the workspace must be a contiguous 1-D CUDA tensor on {device}")
+
+
 def _qkv_check(q, k, v):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -93,6 +110,8 @@ def _qkv_check(q, k, v):
             raise ValueError(f"{name} must be a contiguous 4-D bfloat16 CUDA tensor [B, Hh, N, D]")
     if not (q.shape == k.shape == v.shape):
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
 
 
 def num_cubes(T: int, H: int, W: int) -> int:
@@ -128,7 +147,10 @@ def wf_attn_dense(q, k, v, scale: Optional[float] = None, with_lse: bool = False
         out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=q.device)
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    _expect(out, "out", (B, Hh, N, D), torch.float32, q.device)
+    _expect(lse, "lse", (B, Hh, N), torch.float32, q.device)
     ws = _workspace(dense_workspace_bytes(B, Hh, N, D), q.device, workspace)
+    _expect_workspace(ws, q.device)
     if softmax_mode == WF_SOFTMAX_GUARDED:
         _check(lib.wf_attn_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
                                  B, Hh, N, D, scale, ws.data_ptr(), ws.numel() * ws.element_size(),
@@ -149,14 +171,16 @@ def wf_rope_qk(q, k, grid, theta: float = 10000.0, precision: int = 32, q_out=No
     for name, t in (("q", q), ("k", k)):
         if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
             raise ValueError(f"{name} must be a contiguous 4-D bfloat16 CUDA tensor [B, Hh, N, D]")
-    if q.shape != k.shape:
-        raise ValueError(f"q, k shapes differ: {tuple(q.shape)} {tuple(k.shape)}")
+    if q.shape != k.shape or q.device != k.device:
+        raise ValueError(f"q, k differ: {tuple(q.shape)} on {q.device}, {tuple(k.shape)} on {k.device}")
     T, H, W = grid
     B, Hh, N, D = q.shape
     if N != T * H * W:
         raise ValueError(f"N = {N} but the grid has {T * H * W} tokens")
     q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
+    _expect(q_out, "q_out", q.shape, torch.bfloat16, q.device)
+    _expect(k_out, "k_out", k.shape, torch.bfloat16, q.device)
     _check(lib.wf_rope_qk(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, Hh, T, H, W, D,
                           float(theta), int(precision), _stream_handle(q.device)), "wf_rope_qk")
     return q_out, k_out
@@ -182,7 +206,10 @@ def wf_vsa_coarse_topk(q, k, v, grid, topk: int, scale: Optional[float] = None,
         idx = torch.empty((B, Hh, C, max(topk, 1)), dtype=torch.int32, device=q.device)
     if with_scores and scores is None:
         scores = torch.empty((B, Hh, C, C), dtype=torch.float32, device=q.device)
+    _expect(idx, "idx", (B, Hh, C, max(topk, 1)), torch.int32, q.device)  # topk < 1: the library says why
+    _expect(scores, "scores", (B, Hh, C, C), torch.float32, q.device)
     ws = _workspace(vsa_workspace_bytes(B, Hh, T, H, W, D), q.device, workspace)
+    _expect_workspace(ws, q.device)
     if rope_theta is None:
         _check(lib.wf_vsa_coarse_topk(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D, scale,
                                       topk, idx.data_ptr(), _ptr(scores), ws.data_ptr(),
@@ -206,13 +233,19 @@ def wf_vsa_fine(workspace, idx, shape, grid, scale: Optional[float] = None, with
     torch = _torch()
     B, Hh, N, D = shape
     T, H, W = grid
-    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 4:
+    if idx.dim() != 4:
         raise ValueError("idx must be a contiguous int32 tensor [B, Hh, C, topk]")
+    if N != T * H * W:
+        raise ValueError(f"N = {N} but the grid has {T * H * W} tokens")
+    _expect(idx, "idx", (B, Hh, num_cubes(T, H, W), idx.shape[3]), torch.int32, idx.device)
+    _expect_workspace(workspace, idx.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=idx.device)
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=idx.device)
+    _expect(out, "out", (B, Hh, N, D), torch.float32, idx.device)
+    _expect(lse, "lse", (B, Hh, N), torch.float32, idx.device)
     if softmax_mode == WF_SOFTMAX_GUARDED:
         _check(lib.wf_vsa_fine(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                idx.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3], out.data_ptr(),
@@ -235,17 +268,25 @@ def wf_vsa_fine_gated(workspace, idx, gate, grid, scale: Optional[float] = None,
     torch = _torch()
     if not gate.is_cuda or gate.dtype != torch.bfloat16 or not gate.is_contiguous() or gate.dim() != 4:
         raise ValueError("gate must be a contiguous 4-D bfloat16 CUDA tensor [B, Hh, N, D]")
-    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 4:
+    if idx.dim() != 4:
         raise ValueError("idx must be a contiguous int32 tensor [B, Hh, C, topk]")
     B, Hh, N, D = gate.shape
     T, H, W = grid
+    if N != T * H * W:
+        raise ValueError(f"the gate has N = {N} tokens but the grid has {T * H * W}")
+    C = num_cubes(T, H, W)
+    _expect(idx, "idx", (B, Hh, C, idx.shape[3]), torch.int32, gate.device)
+    _expect_workspace(workspace, gate.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=gate.device)
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=gate.device)
     if with_coarse and o_coarse is None:
-        o_coarse = torch.empty((B, Hh, num_cubes(T, H, W), D), dtype=torch.float32, device=gate.device)
+        o_coarse = torch.empty((B, Hh, C, D), dtype=torch.float32, device=gate.device)
+    _expect(out, "out", (B, Hh, N, D), torch.float32, gate.device)
+    _expect(lse, "lse", (B, Hh, N), torch.float32, gate.device)
+    _expect(o_coarse, "o_coarse", (B, Hh, C, D), torch.float32, gate.device)
     _check(lib.wf_vsa_fine_gated(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                  idx.data_ptr(), gate.data_ptr(), B, Hh, T, H, W, D, scale, idx.shape[3],
                                  out.data_ptr(), _ptr(lse), _ptr(o_coarse), _stream_handle(gate.device)),
@@ -273,7 +314,10 @@ def wf_sta(q, k, v, grid, window, scale: Optional[float] = None, with_lse: bool 
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
     plan = (torch.empty((num_cubes(T, H, W), wt * wh * ww), dtype=torch.int32, device=q.device)
             if with_plan else None)
+    _expect(out, "out", (B, Hh, N, D), torch.float32, q.device)
+    _expect(lse, "lse", (B, Hh, N), torch.float32, q.device)
     ws = _workspace(lib.wf_sta_workspace_bytes(B, Hh, T, H, W, D, wt, wh, ww), q.device, workspace)
+    _expect_workspace(ws, q.device)
     _check(lib.wf_sta(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D, scale, wt, wh, ww,
                       out.data_ptr(), _ptr(lse), _ptr(plan), ws.data_ptr(), ws.numel() * ws.element_size(),
                       _stream_handle(q.device)), "wf_sta")
