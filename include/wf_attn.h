@@ -28,6 +28,10 @@
  *   wf_vsa_fine is the only exception, and it says so).  Work is enqueued on
  *   `stream` (a hipStream_t; NULL means the null stream) in call order.
  *   Calls are reentrant; concurrent calls must use distinct workspaces.
+ *   A call enqueues kernel launches only (no memset, no copy), so calls may
+ *   be captured into a HIP graph and replayed; a replay reads the buffers'
+ *   contents at replay time (WF_VALIDATE=1 and wf_profile_enable(1) are not
+ *   for use under capture: they synchronise or record events).
  *
  *   Errors: every entry point returns a wf_status.  Argument checks run on
  *   the host before anything is enqueued; on failure nothing is enqueued and
