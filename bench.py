@@ -5,10 +5,15 @@ in HBM:
   * dense attention, CFG pair x 40 heads x 32,760 tokens x d128 (one call);
   * VSA, 1 x 40 heads, grid 21x30x52 padded to 624 cubes, top-32: the coarse
     call (gather + pool, scores, top-k) and the fine call.
-Prints one JSON line.  The per-kernel times come from HIP events the library
-records on the launch stream around each kernel.  After the timed steps two
-extra records are taken (not part of the step): VSA at top-78, and the step's
-kernels on one GPU's share of the heads when eight GPUs split them.
+Prints one JSON line.  ms_per_step is the time of exactly --steps steps over
+their count.  The per-kernel times are means over those steps, from HIP events
+the library records on the launch stream around each kernel; the per-call
+medians come from events recorded on the same stream around each call.  After
+the timed steps, extra records are taken (not part of the step): VSA at
+top-78, VSA with the gated coarse branch, the 3D RoPE (standalone and fused),
+the softmax reference policies, sliding-tile attention, the 720p shape, and
+the step's kernels on one GPU's share of the heads when eight GPUs split them
+(--no-extra skips them).
 """
 from __future__ import annotations
 
@@ -201,10 +206,19 @@ def main():
                        device=dev)
     grid = (wv.T, wv.H, wv.W)
 
-    def step():
+    def step(ev=None):
+        # ev: four events recorded on the launch stream around the step's three calls
+        if ev:
+            ev[0].record()
         wf.wf_attn_dense(qd, kd, vd, out=od, workspace=ws_d)
+        if ev:
+            ev[1].record()
         wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
+        if ev:
+            ev[2].record()
         wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
+        if ev:
+            ev[3].record()
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -219,14 +233,18 @@ def main():
     wf.profile_enable(True)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(call_ev[i])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
+    # per-call medians over the timed steps (the means come from the library's per-kernel events)
+    per_call = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(3)] for ev in call_ev])
+    med_dense, med_coarse, med_fine = (float(np.median(per_call[:, j])) for j in range(3))
     kern = {}
     for name in ("wf_transpose_v", "wf_dense_fwd", "wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk",
                  "wf_vsa_fine"):
@@ -501,6 +519,7 @@ def main():
             "frac_peak_at_profiled_clock": (dense_tf / (PEAK_BF16_TFLOPS * counters["clock_ghz"] / PEAK_CLOCK_GHZ)
                                             if counters.get("clock_ghz") else None),
             "ms_per_call": ms_dense,
+            "ms_per_call_median": med_dense,
             "kernel_ms": {"wf_transpose_v": kern["wf_transpose_v"], "wf_dense_fwd": kern["wf_dense_fwd"]},
             "tflops_call": fl_d / (ms_dense * 1e-3) / 1e12,
             "tflops_kernel": dense_tf,
@@ -509,6 +528,9 @@ def main():
         },
         "vsa": {
             "ms_per_call": ms_vsa,
+            "ms_per_call_median": med_coarse + med_fine,
+            "coarse_call_ms_median": med_coarse,
+            "fine_call_ms_median": med_fine,
             "kernel_ms": {k: kern[k] for k in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine")},
             "fine_tflops": fl_v["fine"] / (kern["wf_vsa_fine"] * 1e-3) / 1e12,
             "fine_tflops_padded_queries": fl_v["fine"] * C * 64 / wv.N / (kern["wf_vsa_fine"] * 1e-3) / 1e12,
