@@ -1,13 +1,15 @@
-"""Seeded random sweep of shapes and scales, dense and VSA, against the fp64 oracle.
+"""Seeded random sweep of every entry point against the fp64 oracle.
 
 The hand-picked parity cases cover the tile edges and the measured shapes;
-this sweep draws further cases from a fixed seed (so the list is the same on
+this sweep draws further cases from fixed seeds (so the list is the same on
 every run and each case is named in the test id): token counts and grids of
 every size up to a few thousand tokens, both head dimensions, batch and head
-counts above one, both input recipes, any top-k from 1 to all cubes, and the
-caller's own softmax scale on half of the cases (every other test uses
-1/sqrt(D)).  Every output is compared: O and lse on all rows, the coarse
-scores, and the selected cubes exactly under the near-tie rule.
+counts above one, both input recipes, any top-k from 1 to all cubes, any
+sliding-tile window that fits the cube grid, random gates, RoPE frequency
+bases from 1e2 to 1e6 in both precisions, and the caller's own softmax scale
+on half of the attention cases (every other test uses 1/sqrt(D)).  Every
+output is compared: O and lse on all rows, the coarse scores, the selected
+cubes exactly under the near-tie rule, the STA plan and the RoPE bits exactly.
 """
 import numpy as np
 import pytest
@@ -114,3 +116,109 @@ def test_vsa_sweep(wf, case):
         assert_close(o[b, h][m], o_ref[m], f"fine O b{b} h{h} ({m.sum()} rows)")
         assert errors(lse[b, h][m], l_ref[m])[0] <= LSE_MAX_ABS
     print(f"  near-tie rows: {near}", flush=True)
+
+
+def _sta_cases(n=6, seed=2028):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T, H, W = (int(x) for x in r.integers(1, 17, size=3))
+        nt, nh, nw = (T + 3) // 4, (H + 3) // 4, (W + 3) // 4
+        window = (int(r.integers(1, nt + 1)), int(r.integers(1, nh + 1)), int(r.integers(1, nw + 1)))
+        scale = None if i % 2 == 0 else round(float(r.uniform(0.03, 0.15)), 4)
+        out.append(dict(grid=(T, H, W), window=window, B=int(r.integers(1, 3)), Hh=int(r.integers(1, 3)),
+                        scale=scale, seed=3000 + i))
+    return out
+
+
+def _gated_cases(n=5, seed=2029):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T, H, W = (int(x) for x in r.integers(1, 14, size=3))
+        C = ((T + 3) // 4) * ((H + 3) // 4) * ((W + 3) // 4)
+        scale = None if i % 2 == 0 else round(float(r.uniform(0.03, 0.15)), 4)
+        out.append(dict(grid=(T, H, W), topk=int(r.integers(1, C + 1)), Hh=int(r.integers(1, 3)), scale=scale,
+                        seed=4000 + i))
+    return out
+
+
+def _rope_cases(n=8, seed=2030):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        grid = tuple(int(x) for x in r.integers(1, 20, size=3))
+        theta = 10000.0 if i % 2 == 0 else round(float(10 ** r.uniform(2, 6)), 1)
+        out.append(dict(grid=grid, D=int(r.choice([64, 128])), Hh=int(r.integers(1, 4)), theta=theta,
+                        precision=(32, 64)[(i // 2) % 2], seed=5000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _sta_cases(), ids=_id)
+def test_sta_sweep(wf, case):
+    import torch
+    T, H, W = case["grid"]
+    B, Hh, window = case["B"], case["Hh"], case["window"]
+    wl = synth.small_workload("sweep_sta", B, Hh, T, H, W, 128, structured=True, seed=case["seed"], window=window)
+    scale = wl.scale if case["scale"] is None else case["scale"]
+    log(f"sta sweep {case}")
+    q, k, v = synth.make_qkv(wl)
+    o, lse, plan = wf.wf_sta(to_device(q), to_device(k), to_device(v), (T, H, W), window, scale=case["scale"],
+                             with_lse=True, with_plan=True)
+    torch.cuda.synchronize()
+    o, lse, plan = o.cpu().numpy(), lse.cpu().numpy(), plan.cpu().numpy()
+    assert np.array_equal(plan, oracle.sta_plan(T, H, W, window)), "plan differs from the oracle's"
+    tok = oracle.cube_layout(T, H, W)
+    heads = [(b, h) for b in range(B) for h in range(Hh)]
+
+    def one(bh):
+        b, h = bh
+        return oracle.sta(*(synth.bits_to_f64(x[b, h]) for x in (q, k, v)), tok, T, H, W, window, scale)
+    for (b, h), (o_ref, l_ref) in zip(heads, pmap(one, heads)):
+        m = ~np.isnan(l_ref)
+        assert_close(o[b, h][m], o_ref[m], f"STA O b{b} h{h} ({m.sum()} rows)")
+        assert errors(lse[b, h][m], l_ref[m])[0] <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("case", _gated_cases(), ids=_id)
+def test_gated_sweep(wf, case):
+    import torch
+    T, H, W = case["grid"]
+    Hh, topk = case["Hh"], case["topk"]
+    wl = synth.small_workload("sweep_gated", 1, Hh, T, H, W, 128, structured=True, seed=case["seed"], topk=topk)
+    scale = wl.scale if case["scale"] is None else case["scale"]
+    log(f"gated sweep {case}")
+    q, k, v = synth.make_qkv(wl)
+    gate = synth.make_gate(wl)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    idx, _, ws = wf.wf_vsa_coarse_topk(qd, kd, vd, (T, H, W), topk, scale=case["scale"])
+    o, lse, _ = wf.wf_vsa_fine_gated(ws, idx, to_device(gate), (T, H, W), scale=case["scale"], with_lse=True)
+    torch.cuda.synchronize()
+    idx, o, lse = idx.cpu().numpy(), o.cpu().numpy(), lse.cpu().numpy()
+    tok = oracle.cube_layout(T, H, W)
+
+    def one(h):
+        qf, kf, vf = (synth.bits_to_f64(x[0, h]) for x in (q, k, v))
+        return oracle.gated(qf, kf, vf, tok, idx[0, h], scale, synth.bits_to_f64(gate[0, h]))
+    for h, (o_ref, l_ref) in zip(range(Hh), pmap(one, list(range(Hh)))):
+        m = ~np.isnan(l_ref)
+        assert_close(o[0, h][m], o_ref[m], f"gated O h{h} ({m.sum()} rows)")
+        assert errors(lse[0, h][m], l_ref[m])[0] <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("case", _rope_cases(), ids=_id)
+def test_rope_sweep(wf, case):
+    import torch
+    T, H, W = case["grid"]
+    wl = synth.small_workload("sweep_rope", 1, case["Hh"], T, H, W, case["D"], structured=True, seed=case["seed"])
+    log(f"rope sweep {case}")
+    q, k, _ = synth.make_qkv(wl)
+    qr, kr = wf.wf_rope_qk(to_device(q), to_device(k), (T, H, W), case["theta"], case["precision"])
+    torch.cuda.synchronize()
+    prec = {32: "fp32", 64: "fp64"}[case["precision"]]
+    for name, got, x in (("q", qr, q), ("k", kr, k)):
+        bits = got.view(torch.int16).cpu().numpy().view(np.uint16)
+        for h in range(case["Hh"]):
+            ref = oracle.rope_bf16(synth.bits_to_f64(x[0, h]), T, H, W, case["theta"], prec)
+            want = synth.bf16_bits(ref.astype(np.float32))  # bf16-valued: exact in fp32
+            assert np.array_equal(bits[0, h], want), f"{name} h{h}: RoPE bits differ from the oracle's"
