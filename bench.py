@@ -76,6 +76,9 @@ def parse():
                    help="skip timing the CPU oracle (used for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--traffic-json", metavar="ROCPROF_DIR", default=None,
+                   help="write the dense kernel's calibrated traffic, clock and MFMA busy fraction from a "
+                        "rocprofv3 run directory to profiles/ and exit (no GPU)")
     p.add_argument("--summarize", metavar="ROCPROF_DIR", default=None,
                    help="print a text summary of rocprofv3 CSV output under ROCPROF_DIR and exit")
     p.add_argument("--no-extra", action="store_true",
@@ -172,10 +175,59 @@ def summarize(rocprof_dir: str) -> None:
             print(f"{k[:44]:44s} n={len(next(iter(cs.values())))}  {vals}")
 
 
+def write_traffic(rocprof_dir: str) -> None:
+    """Write TRAFFIC_FILE from a rocprofv3 run directory (no GPU needed).
+
+    The directory holds the passes the committed profiles name: kt/ (kernel
+    trace), FETCH_SIZE/ and WRITE_SIZE/ (one --pmc counter each) and sq1/
+    (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES), all of the same bench command
+    with --copy-probe-mib 1024.  The 1 GiB device copy in that command
+    calibrates the byte counters: each is scaled so that the copy reads as 1 GiB
+    fetched and 1 GiB written.
+    """
+    def counter(run, name, kern):
+        path = os.path.join(rocprof_dir, run, f"{run}_counter_collection.csv")
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if kern in r["Kernel_Name"] and r["Counter_Name"] == name]
+        if not vals:
+            raise SystemExit(f"{path}: no {name} for {kern}")
+        return sum(vals) / len(vals)
+
+    def avg_ms(kern):
+        for r in csv.DictReader(open(os.path.join(rocprof_dir, "kt", "kt_kernel_stats.csv"))):
+            if kern in r["Name"]:
+                return float(r["AverageNs"]) / 1e6
+        raise SystemExit(f"no {kern} in the kernel trace")
+
+    copy, kern = "__amd_rocclr_copyBuffer", "wf_dense_fwd"
+    cf, cw = counter("FETCH_SIZE", "FETCH_SIZE", copy), counter("WRITE_SIZE", "WRITE_SIZE", copy)
+    fs, ws = round((1 << 30) / (cf * 1024), 2), round((1 << 30) / (cw * 1024), 2)
+    fe, wr = counter("FETCH_SIZE", "FETCH_SIZE", kern), counter("WRITE_SIZE", "WRITE_SIZE", kern)
+    gui = counter("sq1", "GRBM_GUI_ACTIVE", kern)            # summed over the 8 XCDs
+    busy = counter("sq1", "SQ_VALU_MFMA_BUSY_CYCLES", kern)  # summed over the 1,024 SIMDs
+    out = {"kernel": kern, "workload": "dense MHA 2x40x32760xd128",
+           "source_sha256": sources_sha256(DENSE_SOURCES),
+           "clock_ghz": round(gui / 8 / (avg_ms(kern) * 1e-3) / 1e9, 3),
+           "mfma_busy": round(busy / 1024 / (gui / 8), 3),
+           "fetch_kib_per_dispatch": round(fe, 2), "write_kib_per_dispatch": round(wr, 2),
+           "calibration": {"copy_bytes": 1 << 30, "copy_fetch_kib": round(cf), "copy_write_kib": round(cw),
+                           "fetch_scale": fs, "write_scale": ws},
+           "bytes_per_launch": fe * 1024 * fs + wr * 1024 * ws,
+           "summary": "profiles/hbm_bytes_dense_2x40x32760_vsa_1x40_top32.txt",
+           "command": "python3 bench.py --traffic-json <rocprofv3 run directory>"}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.traffic_json:
+        write_traffic(args.traffic_json)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py times one GPU (one GPU's share of the heads): --gpus must be 1",
