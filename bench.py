@@ -175,8 +175,8 @@ def summarize(rocprof_dir: str) -> None:
             print(f"{k[:44]:44s} n={len(next(iter(cs.values())))}  {vals}")
 
 
-def write_traffic(rocprof_dir: str) -> None:
-    """Write TRAFFIC_FILE from a rocprofv3 run directory (no GPU needed).
+def write_traffic(rocprof_dir: str, out_path: str = TRAFFIC_FILE) -> dict:
+    """Write the traffic summary (TRAFFIC_FILE) from a rocprofv3 run directory (no GPU needed).
 
     The directory holds the passes the committed profiles name: kt/ (kernel
     trace), FETCH_SIZE/ and WRITE_SIZE/ (one --pmc counter each) and sq1/
@@ -215,10 +215,10 @@ def write_traffic(rocprof_dir: str) -> None:
            "bytes_per_launch": fe * 1024 * fs + wr * 1024 * ws,
            "summary": "profiles/hbm_bytes_dense_2x40x32760_vsa_1x40_top32.txt",
            "command": "python3 bench.py --traffic-json <rocprofv3 run directory>"}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    print(json.dumps(out))
+    return out
 
 
 def main():
@@ -227,7 +227,7 @@ def main():
         summarize(args.summarize)
         return
     if args.traffic_json:
-        write_traffic(args.traffic_json)
+        print(json.dumps(write_traffic(args.traffic_json)))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py times one GPU (one GPU's share of the heads): --gpus must be 1",

@@ -39,3 +39,35 @@ def test_summarize_reads_rocprof_csv(tmp_path):
     assert r.returncode == 0, r.stderr
     assert "37.0000" in r.stdout and "36.0000" in r.stdout and "39.0000" in r.stdout
     assert "FETCH_SIZE=200" in r.stdout and "n=2" in r.stdout
+
+
+def _counter_csv(path, rows):
+    path.mkdir()
+    with open(path / f"{path.name}_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerows(rows)
+
+
+def test_traffic_json_calibrates_against_the_copy(tmp_path):
+    """Known counter values in, the derived bytes, clock and MFMA busy fraction out."""
+    sys.path.insert(0, ROOT)
+    import bench
+    dense, copy = "void wf::wf_dense_fwd<128, 0>(unsigned short const*)", "__amd_rocclr_copyBuffer"
+    (tmp_path / "kt").mkdir()
+    with open(tmp_path / "kt" / "kt_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow([dense, 2, 80e6, 40e6, 99.0, 40e6, 40e6, 0])
+    # the 1 GiB copy reads as half its bytes fetched and all of them written: scales 2 and 1
+    _counter_csv(tmp_path / "FETCH_SIZE", [[copy, "FETCH_SIZE", 524288], [dense, "FETCH_SIZE", 1e6],
+                                           [dense, "FETCH_SIZE", 1e6]])
+    _counter_csv(tmp_path / "WRITE_SIZE", [[copy, "WRITE_SIZE", 1048576], [dense, "WRITE_SIZE", 5e5]])
+    # 2 GHz over a 40 ms launch on 8 XCDs; the matrix pipe busy half of the cycles on 1,024 SIMDs
+    _counter_csv(tmp_path / "sq1", [[dense, "GRBM_GUI_ACTIVE", 8 * 2e9 * 0.04],
+                                    [dense, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * 2e9 * 0.04]])
+    out = bench.write_traffic(str(tmp_path), str(tmp_path / "traffic.json"))
+    assert out["calibration"]["fetch_scale"] == 2.0 and out["calibration"]["write_scale"] == 1.0
+    assert out["bytes_per_launch"] == 1e6 * 1024 * 2 + 5e5 * 1024
+    assert out["clock_ghz"] == 2.0 and out["mfma_busy"] == 0.5
+    assert json.load(open(tmp_path / "traffic.json")) == out
