@@ -54,8 +54,9 @@ __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict
 // the slot K(t-1) left and half B copies V(t+2) into the slot V(t-1) left, so
 // the copy work is split evenly over the two halves; each waits for its copies
 // at the end of its next MFMA phase, so each copy has a phase to land.  Within an MFMA phase the
-// LDS operand reads run four MFMAs ahead of use; the first four are read at the
-// end of the wavefront's VALU phase, before the barrier.  SM selects the
+// LDS operand reads run four MFMAs ahead of use; the first four are read early in
+// the wavefront's VALU phase, right after its copies, so their latency hides behind the
+// softmax.  SM selects the
 // softmax reference policy (softmax_tile; the library default is the guarded
 // integer reference).
 template <int D, int SM>
@@ -124,9 +125,9 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   //     (2t+3) and publishes it from 2t+4; V(t+2) is first read by half A's operand prefetch
   //     at the end of 2t+5.
   // So each copy has one full phase to land, and both halves issue 4 copies per VALU phase.
-  // The first operands of every MFMA phase are read at the end of the wavefront's previous
-  // VALU phase, before the barrier, so the matrix pipe does not idle through the LDS latency
-  // at each phase start.
+  // The first operands of every MFMA phase are read at the start of the wavefront's previous
+  // VALU phase (V(t) was published by the barrier that opened it), so the matrix pipe does not
+  // idle through the LDS latency at each phase start and the reads overlap the softmax.
   uint4 ring[kRing];
   auto phase_pair = [&](auto half_a_c, int t, const char* kcur, const char* vprev, char* knext,
                         const char* vnext) __attribute__((always_inline)) {
@@ -146,6 +147,7 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     else
       tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + (long)(t + 2) * 64, Np,
                       t + 2 < nt ? vbytes - (uint32_t)(t + 2) * 128 : 0u, const_cast<char*>(vprev), wq);
+    mfma_prefill<D, 0>(ring, vnext, kcur, j, half);  // first operands of MFMA phase t+1: V(t) rows
     if (t < nt) {
       if ((t + 1) * 64 > N) {  // ragged last tile: keys >= N do not exist
 #pragma unroll
@@ -156,7 +158,6 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, p2);
     }
-    mfma_prefill<D, 0>(ring, vnext, kcur, j, half);  // first operands of MFMA phase t+1: V(t) rows
     barrier_nofence();
   };
   // unrolled by three so every LDS array is named statically, and instantiated once per half
