@@ -71,3 +71,20 @@ def test_traffic_json_calibrates_against_the_copy(tmp_path):
     assert out["bytes_per_launch"] == 1e6 * 1024 * 2 + 5e5 * 1024
     assert out["clock_ghz"] == 2.0 and out["mfma_busy"] == 0.5
     assert json.load(open(tmp_path / "traffic.json")) == out
+
+
+def test_reported_vsa_flops_follow_the_page_convention():
+    """bench.py's fine-stage FLOPs for the page's 78-of-624 operating point give the
+    page's roofline figure (padded query tokens left out), printed in tests/golden/."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    golden = json.load(open(os.path.join(ROOT, "tests", "golden", "page4_vsa_480p.json")))
+    wl = synth.WORKLOADS["vsa_480p_k78"]
+    assert (wl.T, wl.H, wl.W, wl.Hh, wl.D, wl.topk) == (golden["T"], golden["H"], golden["W"], golden["heads"],
+                                                        golden["head_dim"], golden["kept_cubes"])
+    fl = bench.vsa_flops(wl, golden["cubes"])
+    assert round(fl["fine"] / 1e12, 2) == golden["tflop_rounded"]
+    # the step's own top-32 figure scales with k
+    wl32 = synth.WORKLOADS["vsa_480p"]
+    assert bench.vsa_flops(wl32, golden["cubes"])["fine"] * 78 == fl["fine"] * 32
