@@ -222,3 +222,17 @@ def test_rope_sweep(wf, case):
             ref = oracle.rope_bf16(synth.bits_to_f64(x[0, h]), T, H, W, case["theta"], prec)
             want = synth.bf16_bits(ref.astype(np.float32))  # bf16-valued: exact in fp32
             assert np.array_equal(bits[0, h], want), f"{name} h{h}: RoPE bits differ from the oracle's"
+
+
+def test_extended_sweep(wf):
+    """160 further seeded cases through the same checks (40 dense, 40 VSA, 25 STA, 25 gated,
+    30 RoPE), run in one test; a failure names its case."""
+    plan = [(test_dense_sweep, _dense_cases(40, 7001)), (test_vsa_sweep, _vsa_cases(40, 7002)),
+            (test_sta_sweep, _sta_cases(25, 7003)), (test_gated_sweep, _gated_cases(25, 7004)),
+            (test_rope_sweep, _rope_cases(30, 7005))]
+    for fn, cases in plan:
+        for case in cases:
+            try:
+                fn(wf, case)
+            except AssertionError as e:
+                raise AssertionError(f"{fn.__name__} {case}: {e}") from e
