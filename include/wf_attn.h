@@ -82,7 +82,9 @@ size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D
  *   q, k, v    bf16 [B][Hh][N][D], read only.
  *   o          fp32 [B][Hh][N][D], written.
  *   lse        fp32 [B][Hh][N], written; may be NULL.
- *   N          tokens (T*H*W), 1 <= N < 2^31 / D.
+ *   N          tokens (T*H*W), 1 <= N, and one head's K (N rounded up to 64,
+ *              times D bf16) below 2 GiB: 64*ceil(N/64)*D*2 < 2^31, else
+ *              WF_ERR_UNSUPPORTED (N <= 8,388,544 at D = 128).
  *   D          64 or 128.
  *   scale      finite and > 0 (1/sqrt(D) for the standard operation).
  *   workspace  device scratch of at least wf_attn_dense_workspace_bytes(),

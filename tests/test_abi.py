@@ -69,6 +69,9 @@ def test_dense_argument_errors(wf):
     assert dense(wf, N=0) == 1
     assert dense(wf, B=-1) == 1
     assert dense(wf, N=1 << 24) == 1          # N*D does not fit in int32
+    assert dense(wf, N=1 << 23) == 2          # one head's K reaches 2 GiB (32-bit descriptors)
+    assert dense(wf, N=(1 << 23) - 64) == 3   # just below: accepted, but the workspace is short
+    assert dense(wf, N=1 << 24, D=64) == 2    # the same bound at D = 64
     assert dense(wf, D=96) == 2
     assert dense(wf, scale=float("nan")) == 1
     assert dense(wf, scale=0.0) == 1

@@ -144,6 +144,9 @@ static int32_t dense(const void* q, const void* k, const void* v, float* o, floa
   if (D != 64 && D != 128) return fail(WF_ERR_UNSUPPORTED, "head dimension %d (64 or 128)", D);
   if ((long long)B * Hh * ((N + 63) / 64) >= (1ll << 31))  // the V^T transpose's grid, the largest
     return fail(WF_ERR_UNSUPPORTED, "B=%d Hh=%d N=%d: too many workgroups for one launch", B, Hh, N);
+  // one head's K and V^T are read through buffer descriptors with 32-bit byte counts and offsets
+  if ((long long)((N + 63) / 64) * 64 * D * 2 >= (1ll << 31))
+    return fail(WF_ERR_UNSUPPORTED, "N=%d D=%d: one head's K and V^T must stay below 2 GiB", N, D);
   if (!isfinite(scale) || !(scale > 0.f))
     return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
   const size_t need = wf::dense_workspace_bytes(B * Hh, N, D);
