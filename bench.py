@@ -123,7 +123,12 @@ def vsa_bytes(wl, C) -> dict:
 
 
 def cpu_baseline(seconds: float) -> dict:
-    """The fp64 oracle on a bounded sample of the dense workload: whole heads, about `seconds` of CPU."""
+    """The fp64 oracle on a bounded sample of the step's workload, about `seconds` of CPU.
+
+    Whole dense heads of the dense workload (most of the budget) and whole VSA heads
+    (pool, scores, top-k, fine) of the VSA workload; the rate is the step's FLOPs over
+    the step's time extrapolated from the per-head times, the same convention as
+    `value`."""
     import numpy as np
     import oracle
     import synth
@@ -132,23 +137,33 @@ def cpu_baseline(seconds: float) -> dict:
         threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
     except Exception:
         threads = os.cpu_count() or 1
-    wl = synth.WORKLOADS[DENSE]
-    phi = synth.field_for(wl)
-    heads, dt = 0, 0.0
-    for bh in range(wl.B * wl.Hh):          # whole heads until the time budget is spent
-        b, h = divmod(bh, wl.Hh)
-        q, k, v = (synth.bits_to_f64(synth.make_slice(wl, t, b, h, phi)) for t in ("q", "k", "v"))
-        t0 = time.perf_counter()
-        oracle.attention(q, k, v, wl.scale)
-        dt += time.perf_counter() - t0
-        heads += 1
-        if dt >= seconds:
-            break
-    flops = 4.0 * heads * wl.N * wl.N * wl.D
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle, dense attention of {heads} whole head(s) "
-                      f"({wl.N} x {wl.N} x d{wl.D}) of the {DENSE} workload, {dt:.1f} s; "
-                      f"one full dense call extrapolated: {dt / heads * wl.B * wl.Hh:.0f} s",
+    wd, wv = synth.WORKLOADS[DENSE], synth.WORKLOADS[VSA]
+
+    def heads_within(wl, budget, run, least=1):
+        phi = synth.field_for(wl)
+        n, dt = 0, 0.0
+        for bh in range(wl.B * wl.Hh):          # whole heads until the time budget is spent
+            b, h = divmod(bh, wl.Hh)
+            q, k, v = (synth.bits_to_f64(synth.make_slice(wl, t, b, h, phi)) for t in ("q", "k", "v"))
+            t0 = time.perf_counter()
+            run(wl, q, k, v)
+            dt += time.perf_counter() - t0
+            n += 1
+            if n >= least and dt >= budget:
+                break
+        return n, dt
+
+    nd, td = heads_within(wd, 0.85 * seconds, lambda wl, q, k, v: oracle.attention(q, k, v, wl.scale))
+    nv, tv = heads_within(wv, 0.15 * seconds,
+                          lambda wl, q, k, v: oracle.vsa(q, k, v, wl.T, wl.H, wl.W, wl.topk, wl.scale), least=2)
+    C = int(oracle.geometry(wv.T, wv.H, wv.W)["C"])
+    step_flops = dense_flops(wd) + vsa_flops(wv, C)["total"]
+    step_s = td / nd * wd.B * wd.Hh + tv / nv * wv.B * wv.Hh
+    return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy oracle: dense attention of {nd} whole head(s) ({wd.N} x {wd.N} x d{wd.D}) "
+                      f"of the {DENSE} workload in {td:.1f} s, and the whole VSA pass of {nv} head(s) of the "
+                      f"{VSA} workload (top-{wv.topk} of {C} cubes) in {tv:.1f} s; one step extrapolated: "
+                      f"{step_s:.0f} s",
             "host_cpus": os.cpu_count()}
 
 
