@@ -1,9 +1,9 @@
 """Dense attention on the GPU (through the C ABI) against the fp64 oracle.
 
-Small shapes are compared on every output; the full 480p shapes (12 heads,
-and the CFG pair x 40 heads that the benchmark times) run whole on the GPU
-and are compared on sampled query rows of sampled heads, including the first
-rows, rows around tile boundaries and the ragged tail.
+Small shapes are compared on every output; a D = 64 case over several query
+tiles and a 1M-token head on sampled rows.  Outputs are poisoned (NaN) before
+every call.  The production shapes (12 heads and the CFG pair x 40 heads at
+480p, the CFG pair at 720p) are checked whole in test_parity_full.py.
 """
 import math
 
@@ -27,10 +27,16 @@ def wf():
 
 
 def run_dense(wf, q, k, v, scale=None):
+    """One call on outputs poisoned first (NaN): every row must be written."""
     import torch
-    o, lse = wf.wf_attn_dense(to_device(q), to_device(k), to_device(v), scale=scale, with_lse=True)
+    B, Hh, N, D = q.shape
+    o = torch.full((B, Hh, N, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hh, N), float("nan"), dtype=torch.float32, device="cuda")
+    wf.wf_attn_dense(to_device(q), to_device(k), to_device(v), scale=scale, out=o, lse=lse)
     torch.cuda.synchronize()
-    return o.cpu().numpy(), lse.cpu().numpy()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "output rows never written"
+    return o, lse
 
 
 def oracle_heads(wl, q, k, v, heads, rows=None):
@@ -133,28 +139,6 @@ def test_dense_d64_multi_tile_sampled(wf):
         assert_close(o[bh][rows], ref[bh][0], f"O b{bh[0]} h{bh[1]} ({rows.size} rows)")
         assert errors(lse[bh][rows], ref[bh][1])[0] <= LSE_MAX_ABS
     assert np.isfinite(o).all()
-
-
-@pytest.mark.parametrize("name,heads", [("dense_480p_12h", [(0, 0), (0, 5), (0, 11)]),
-                                        ("dense_480p_cfg", [(0, 0), (0, 39), (1, 7), (1, 22)]),
-                                        ("dense_720p_cfg", [(0, 1), (1, 30)])])
-def test_dense_full_shape_sampled(wf, name, heads):
-    wl = synth.WORKLOADS[name]
-    log(f"dense {name} B={wl.B} Hh={wl.Hh} N={wl.N} D={wl.D} (full launch, sampled rows)")
-    q, k, v = synth.make_qkv(wl)
-    o, lse = run_dense(wf, q, k, v)
-    rows = sample_rows(wl.N, np.random.default_rng(wl.seed))
-    ref = oracle_heads(wl, q, k, v, heads, rows)
-    for bh in heads:
-        assert_close(o[bh][rows], ref[bh][0], f"O b{bh[0]} h{bh[1]} ({rows.size} rows)")
-        assert errors(lse[bh][rows], ref[bh][1])[0] <= LSE_MAX_ABS
-    # every head: a handful of rows, and everything finite
-    assert np.isfinite(o).all()
-    few = np.array([0, wl.N // 3, wl.N - 1])
-    allh = [(b, h) for b in range(wl.B) for h in range(wl.Hh)]
-    ref_all = oracle_heads(wl, q, k, v, allh, few)
-    for bh in allh:
-        assert_close(o[bh][few], ref_all[bh][0], f"O b{bh[0]} h{bh[1]} 3 rows")
 
 
 def test_dense_long_ragged_sampled(wf):

@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 import synth
-from wf_testutil import LSE_MAX_ABS, assert_close, check_topk_rows, errors, log, pmap, to_device
+from wf_testutil import (LSE_MAX_ABS, assert_close, check_coarse_scores, check_topk_rows, errors, log, pmap,
+                         to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,7 +111,7 @@ def test_vsa_sweep(wf, case):
         return sc, ridx, margin, tau, o_ref, l_ref
     near = 0
     for (b, h), (sc, ridx, margin, tau, o_ref, l_ref) in zip(heads, pmap(one, heads)):
-        assert np.abs(scores[b, h] - sc).max() <= tau.max() / 4, f"coarse scores b{b} h{h}"
+        check_coarse_scores(scores[b, h], sc, tau, f"coarse scores b{b} h{h}")
         near += check_topk_rows(idx[b, h], sc, ridx, margin, tau)
         m = ~np.isnan(l_ref)
         assert_close(o[b, h][m], o_ref[m], f"fine O b{b} h{h} ({m.sum()} rows)")

@@ -3,7 +3,8 @@
 Checks the selected key-cube indices (exactly, under the near-tie rule), the
 fine-stage output (the GPU's whole pipeline, and the fine stage alone on the
 GPU's own plan), the closed forms (Q = 0 ties, top-k = all cubes equals
-dense attention) and the error paths.
+dense attention) and the error paths.  Outputs are poisoned before every call.
+The 480p and 720p workloads are checked whole in test_parity_full.py.
 """
 import os
 
@@ -12,8 +13,8 @@ import pytest
 
 import oracle
 import synth
-from wf_testutil import (LSE_MAX_ABS, assert_close, check_topk_rows, errors, log, pmap,
-                         to_device)
+from wf_testutil import (LSE_MAX_ABS, assert_close, check_coarse_scores, check_topk_rows, errors, log,
+                         pmap, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,12 +29,21 @@ def wf():
 
 
 def gpu_vsa(wf, wl, q, k, v, topk=None):
+    """Both stages on outputs poisoned first (NaN, indices -1): every entry must be written."""
     import torch
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
-    idx, scores, ws = wf.wf_vsa_coarse_topk(qd, kd, vd, (wl.T, wl.H, wl.W), topk or wl.topk,
-                                            with_scores=True)
-    o, lse = wf.wf_vsa_fine(ws, idx, tuple(qd.shape), (wl.T, wl.H, wl.W), with_lse=True)
+    topk = topk or wl.topk
+    C = wf.num_cubes(wl.T, wl.H, wl.W)
+    idx = torch.full((wl.B, wl.Hh, C, topk), -1, dtype=torch.int32, device="cuda")
+    sc = torch.full((wl.B, wl.Hh, C, C), float("nan"), dtype=torch.float32, device="cuda")
+    o = torch.full(tuple(qd.shape), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full(tuple(qd.shape[:3]), float("nan"), dtype=torch.float32, device="cuda")
+    idx, scores, ws = wf.wf_vsa_coarse_topk(qd, kd, vd, (wl.T, wl.H, wl.W), topk, with_scores=True,
+                                            idx=idx, scores=sc)
+    o, lse = wf.wf_vsa_fine(ws, idx, tuple(qd.shape), (wl.T, wl.H, wl.W), out=o, lse=lse)
     torch.cuda.synchronize()
+    assert not (idx < 0).any().item() and not torch.isnan(scores).any().item()
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item()
     return dict(idx=idx.cpu().numpy(), scores=scores.cpu().numpy(), o=o.cpu().numpy(),
                 lse=lse.cpu().numpy(), ws=ws, idx_dev=idx)
 
@@ -56,8 +66,8 @@ def check_scores_and_idx(g, ref, heads):
     near = 0
     for bh in heads:
         r = ref[bh]
-        # fp32 scores within the tolerance the top-k rule assumes
-        assert np.abs(g["scores"][bh] - r["scores"]).max(axis=1).max() <= r["tau"].max() / 4
+        # fp32 scores within the tolerance the top-k rule assumes, row by row
+        check_coarse_scores(g["scores"][bh], r["scores"], r["tau"], f"scores b{bh[0]} h{bh[1]}")
         near += check_topk_rows(g["idx"][bh], r["scores"], r["idx"], r["margin"], r["tau"])
     print(f"  near-tie rows: {near} of {len(heads) * g['idx'].shape[2]}", flush=True)
     return near
@@ -125,22 +135,6 @@ def test_vsa_zero_queries_tie_rule(wf):
     assert C == 2 * 3 * 3
 
 
-def test_vsa_480p_full(wf):
-    wl = synth.WORKLOADS["vsa_480p"]
-    log(f"vsa {wl.name} B={wl.B} Hh={wl.Hh} grid {wl.T}x{wl.H}x{wl.W} topk={wl.topk} (all heads idx)")
-    q, k, v = synth.make_qkv(wl)
-    g = gpu_vsa(wf, wl, q, k, v)
-    heads = [(0, h) for h in range(wl.Hh)]
-    ref, tok = coarse_ref(wl, q, k, heads, wl.topk)
-    check_scores_and_idx(g, ref, heads)
-    assert np.isfinite(g["o"]).all()
-    C = tok.shape[0]
-    cubes = sorted(set([0, 1, 12, 13, 103, 104, 311, 520, 622, 623] +
-                       np.random.default_rng(4).choice(C, 24, replace=False).tolist()))
-    check_fine(wl, q, k, v, g, tok, [(0, 0), (0, 17)], cubes)
-    check_fine(wl, q, k, v, g, tok, [(0, 39)])
-
-
 def test_vsa_480p_k78(wf):
     """The review's operating point: 78 of 624 cubes kept."""
     wl = synth.WORKLOADS["vsa_480p_k78"]
@@ -152,21 +146,6 @@ def test_vsa_480p_k78(wf):
     check_scores_and_idx(g, ref, heads)
     cubes = sorted(np.random.default_rng(78).choice(tok.shape[0], 24, replace=False).tolist() + [0, 623])
     check_fine(wl, q, k, v, g, tok, [(0, 5), (0, 33)], cubes)
-
-
-def test_vsa_720p_full(wf):
-    wl = synth.WORKLOADS["vsa_720p"]
-    log(f"vsa {wl.name} B={wl.B} Hh={wl.Hh} grid {wl.T}x{wl.H}x{wl.W} topk={wl.topk} (all heads idx)")
-    q, k, v = synth.make_qkv(wl)
-    g = gpu_vsa(wf, wl, q, k, v)
-    heads = [(b, h) for b in range(wl.B) for h in range(wl.Hh)]
-    ref, tok = coarse_ref(wl, q, k, heads, wl.topk)
-    check_scores_and_idx(g, ref, heads)
-    assert np.isfinite(g["o"]).all()
-    C = tok.shape[0]
-    cubes = sorted(set([0, 19, 20, 239, 240, 719, 1200, 1439] +
-                       np.random.default_rng(5).choice(C, 16, replace=False).tolist()))
-    check_fine(wl, q, k, v, g, tok, [(0, 3), (1, 36)], cubes)
 
 
 def test_vsa_max_cubes(wf):

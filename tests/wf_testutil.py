@@ -1,6 +1,7 @@
 """Helpers shared by the parity tests: device transfer, error statistics, top-k rule."""
 from __future__ import annotations
 
+import math
 import os
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -10,7 +11,16 @@ import numpy as np
 # Parity bar for floating-point outputs (fp32 GPU output vs fp64 oracle, bf16 inputs).
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
-LSE_MAX_ABS = 4e-3
+# lse bar, derived from the arithmetic (test_tolerances.py checks the derivation on the CPU):
+# the kernels weight V by the bf16-rounded probabilities and normalise by their sum, so O uses
+# one consistent set of weights and the natural-log normaliser they report is the log of that
+# same sum (plus the reference).  bf16 keeps 8 significant bits, so round to nearest moves each
+# p_j by a relative 2^-8 at most, hence the sum as well: the reported lse is within
+# ln(1 + 2^-8) = 3.90e-3 of the exact one.  Rows dominated by one key come close to that
+# (3.2e-3 on the benchmark's inputs), so no bar near 1e-3 can hold for these weights.  The
+# fp32 parts (scores from D bf16 products, worst-case gamma_D bound; exponentials; the running
+# sum over 75,600 keys) add under 6e-4 at the shapes tested; the bar is the sum of the two.
+LSE_MAX_ABS = math.log1p(2.0 ** -8) + 6e-4
 
 
 def log(msg: str) -> None:
@@ -45,6 +55,16 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, m
     mx, mn = errors(gpu, ref)
     print(f"  {what}: max-abs {mx:.3e} mean-abs {mn:.3e}", flush=True)
     assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
+
+
+def check_coarse_scores(gpu: np.ndarray, ref: np.ndarray, tau: np.ndarray, what: str) -> None:
+    """fp32 coarse scores against the fp64 ones, row by row: row c within tau_c / 4, the
+    bound oracle.near_tie_tolerance derives for an fp32 evaluation (and the margin the
+    top-k rule relies on)."""
+    assert gpu.shape == ref.shape
+    err = np.abs(gpu.astype(np.float64) - ref).max(axis=1)
+    bad = np.nonzero(~(err <= tau / 4))[0]
+    assert bad.size == 0, f"{what}: {bad.size} rows beyond tau_c/4, e.g. row {bad[:5]}"
 
 
 def check_topk_rows(gpu_idx: np.ndarray, scores: np.ndarray, ref_idx: np.ndarray,
