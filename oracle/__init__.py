@@ -22,8 +22,9 @@ Sources (cited by page title and section; no code is printed on the pages):
   numerically equivalent Wan kernels", entry fused_rope: a fused 3D RoPE
   with an fp32 or fp64 rotation (oracle/rope.py states the definition
   adopted, since the page gives no frequencies); and, in its approximate
-  attention section, entry "sta", weight-free sliding-tile attention on
-  tuned grids (oracle/sta.py states the tile and window definition adopted).
+  attention section, entry "sta", weight-free sliding-tile attention accepted
+  only on two tuned grids (oracle/sta.py states the 6x8x8 tile and the window
+  definition adopted).
 
 Readings taken where the pages are silent are listed in each function's
 docstring.  All functions take float64 numpy arrays (bf16 inputs widened
@@ -35,11 +36,12 @@ the numbers the pages print; see that file's header for the map.
 """
 from .dense import attention, attention_heads
 from .rope import axis_split, grid_positions, angles, rotate, round_bf16, rope, rope_bf16
-from .sta import window_start, sta_plan, sta
+from .sta import TILE, TUNED_GRIDS, tile_grid, tile_tokens, window_start, sta_plan, sta
 from .vsa import (CUBE, geometry, cube_layout, pool, coarse_scores, select_topk,
                   near_tie_tolerance, fine, vsa, coarse_output, gated, flops_fine, kv_stream_bytes)
 
 __all__ = ["attention", "attention_heads", "CUBE", "geometry", "cube_layout", "pool",
            "coarse_scores", "select_topk", "near_tie_tolerance", "fine", "vsa",
            "coarse_output", "gated", "flops_fine", "kv_stream_bytes", "axis_split", "grid_positions",
-           "angles", "rotate", "round_bf16", "rope", "rope_bf16", "window_start", "sta_plan", "sta"]
+           "angles", "rotate", "round_bf16", "rope", "rope_bf16", "TILE", "TUNED_GRIDS", "tile_grid",
+           "tile_tokens", "window_start", "sta_plan", "sta"]

@@ -34,12 +34,15 @@ Map of pins (function -> what fixes it):
   fp32 rounding steps of the fp64 rotation, and its bf16 rounding agrees
   with the fp64 mode's except on a sliver of near-ties (never by more than
   one bf16 step).
-* oracle.sta_plan / sta (sliding-tile attention, adopted definition): the
-  plan against its geometric definition cube by cube (window size, own cube
-  inside, centred where it fits, pushed inward at edges); the output against
-  a token-level brute force (an explicit allowed-key mask built from token
-  coordinates, softmax by math.exp); a window covering the whole cube grid
-  reduces to dense attention; a 1x1x1 window to attention within each cube.
+* oracle.tile_grid / tile_tokens / sta_plan / sta (sliding-tile attention,
+  adopted definition): the 6x8x8 tile divides both grids the page accepts
+  and not the default grid it refuses; tiles partition the grid row-major;
+  the plan against its geometric definition tile by tile (window size, own
+  tile inside, centred where it fits, pushed inward at edges); the output
+  against a token-level brute force (an allowed-key mask built from token
+  coordinates alone, and plain math.exp loops on some rows); a window
+  covering the whole tile grid reduces to dense attention; a 1x1x1 window to
+  attention within each tile.
 * oracle.round_bf16: matches the float32 round-to-nearest-even of synth on
   float32-representable values, resolves exact ties to even, and rounds fp64
   values just above a tie upward (where an fp32 intermediate would not).
@@ -603,8 +606,30 @@ def test_rope_fp32_mode():
 
 # --------------------------------------------------------------- sliding-tile attention
 
+def test_sta_tile_reading_matches_the_pages_accept_rule():
+    """The 6x8x8 tile divides both grids the page accepts and not the default grid it refuses."""
+    for g in oracle.TUNED_GRIDS:
+        nt, nh, nw = oracle.tile_grid(*g)
+        assert (nt * 6, nh * 8, nw * 8) == g
+    assert oracle.tile_grid(36, 48, 48) == (6, 6, 6) and oracle.tile_grid(18, 48, 80) == (3, 6, 10)
+    with pytest.raises(ValueError):
+        oracle.tile_grid(31, 22, 40)
+
+
+def test_sta_tile_tokens_layout():
+    T, H, W = 12, 16, 24                          # tile grid 2 x 2 x 3
+    tok = oracle.tile_tokens(T, H, W)
+    assert tok.shape == (12, 384)
+    assert np.array_equal(np.sort(tok.ravel()), np.arange(T * H * W))      # a partition of the grid
+    for tile in (0, 5, 11):
+        tt, th, tw = tile // 6, (tile // 3) % 2, tile % 3
+        t, h, w = tok[tile] // (H * W), (tok[tile] // W) % H, tok[tile] % W
+        assert (t // 6 == tt).all() and (h // 8 == th).all() and (w // 8 == tw).all()
+        assert (np.diff(tok[tile]) > 0).all()                                # row-major inside the tile
+
+
 def test_sta_plan_geometry():
-    T, H, W = 13, 10, 23                          # cube grid 4 x 3 x 6
+    T, H, W = 24, 24, 48                          # tile grid 4 x 3 x 6
     plan = oracle.sta_plan(T, H, W, (3, 3, 3))
     nt, nh, nw = 4, 3, 6
     assert plan.shape == (72, 27)
@@ -624,42 +649,57 @@ def test_sta_plan_geometry():
     assert oracle.window_start(9, 4, 10) == 6
     with pytest.raises(ValueError):
         oracle.sta_plan(T, H, W, (5, 1, 1))
+    with pytest.raises(ValueError):
+        oracle.sta_plan(25, H, W, (1, 1, 1))
+
+
+def _sta_mask_brute(T, H, W, window):
+    """allowed[i, j]: key token j lies in query token i's window, from token coordinates alone."""
+    N = T * H * W
+    n = np.arange(N)
+    coords = np.stack([n // (H * W) // 6, (n // W) % H // 8, n % W // 8], 1)
+    tiles = (T // 6, H // 8, W // 8)
+    allowed = np.ones((N, N), dtype=bool)
+    for axis in range(3):
+        c, w, nt = coords[:, axis], window[axis], tiles[axis]
+        lo = np.minimum(np.maximum(c - (w - 1) // 2, 0), nt - w)
+        allowed &= (coords[None, :, axis] >= lo[:, None]) & (coords[None, :, axis] < lo[:, None] + w)
+    return allowed
 
 
 def test_sta_token_brute_force():
-    T, H, W, D = 6, 5, 9, 8                       # cube grid 2 x 2 x 3, ragged on every axis
-    q, k, v = small_vsa_inputs(95, T, H, W, D)
-    tok = oracle.cube_layout(T, H, W)
-    s = 1 / math.sqrt(D)
-    window = (1, 2, 2)
-    o, lse = oracle.sta(q, k, v, tok, T, H, W, window, s)
-    nt, nh, nw = 2, 2, 3
+    T, H, W, D = 12, 8, 24, 8                     # tile grid 2 x 1 x 3
     N = T * H * W
-    for i in range(N):
-        ti, hi, wi = i // (H * W), (i // W) % H, i % W
-        ct, ch, cw = ti // 4, hi // 4, wi // 4
-        lo = [oracle.window_start(c, w, n) for c, w, n in ((ct, 1, nt), (ch, 2, nh), (cw, 2, nw))]
-        allowed = [j for j in range(N)
-                   if lo[0] <= j // (H * W) // 4 < lo[0] + 1 and lo[1] <= (j // W) % H // 4 < lo[1] + 2
-                   and lo[2] <= j % W // 4 < lo[2] + 2]
-        e = [math.exp(s * float(q[i] @ k[j])) for j in allowed]
-        tot = sum(e)
-        ref = sum(w_ * v[j] for w_, j in zip(e, allowed)) / tot
+    r = np.random.default_rng(95)
+    q, k, v = (r.standard_normal((N, D)) for _ in range(3))
+    s = 1 / math.sqrt(D)
+    window = (1, 1, 2)
+    o, lse = oracle.sta(q, k, v, T, H, W, window, s)
+    allowed = _sta_mask_brute(T, H, W, window)
+    assert (allowed.sum(axis=1) == 2 * 384).all()
+    sc = np.where(allowed, (q @ k.T) * s, -np.inf)
+    e = np.exp(sc - sc.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(o, (e @ v) / e.sum(axis=1, keepdims=True), atol=1e-12)
+    np.testing.assert_allclose(lse, sc.max(axis=1) + np.log(e.sum(axis=1)), atol=1e-12)
+    for i in r.choice(N, 12, replace=False):      # a few rows by plain loops
+        js = [j for j in range(N) if allowed[i, j]]
+        ex = [math.exp(s * float(q[i] @ k[j])) for j in js]
+        ref = sum(w_ * v[j] for w_, j in zip(ex, js)) / sum(ex)
         np.testing.assert_allclose(o[i], ref, atol=1e-12)
-        assert abs(lse[i] - math.log(tot)) < 1e-12
+        assert abs(lse[i] - math.log(sum(ex))) < 1e-12
 
 
 def test_sta_closed_forms():
-    T, H, W, D = 7, 9, 6, 16                      # cube grid 2 x 3 x 2
-    q, k, v = small_vsa_inputs(96, T, H, W, D)
-    tok = oracle.cube_layout(T, H, W)
+    T, H, W, D = 12, 16, 8, 16                    # tile grid 2 x 2 x 1
+    r = np.random.default_rng(96)
+    q, k, v = (r.standard_normal((T * H * W, D)) for _ in range(3))
     s = 1 / math.sqrt(D)
-    o, lse = oracle.sta(q, k, v, tok, T, H, W, (2, 3, 2), s)     # the whole cube grid
+    o, lse = oracle.sta(q, k, v, T, H, W, (2, 2, 1), s)          # the whole tile grid
     od, ld = oracle.attention(q, k, v, s)
     np.testing.assert_allclose(o, od, atol=1e-12)
     np.testing.assert_allclose(lse, ld, atol=1e-12)
-    o1, _ = oracle.sta(q, k, v, tok, T, H, W, (1, 1, 1), s)      # each cube on its own
+    o1, _ = oracle.sta(q, k, v, T, H, W, (1, 1, 1), s)           # each tile on its own
+    tok = oracle.tile_tokens(T, H, W)
     for c in range(tok.shape[0]):
-        rows = tok[c][tok[c] >= 0]
-        ob, _ = oracle.attention(q[rows], k[rows], v[rows], s)
-        np.testing.assert_allclose(o1[rows], ob, atol=1e-12)
+        ob, _ = oracle.attention(q[tok[c]], k[tok[c]], v[tok[c]], s)
+        np.testing.assert_allclose(o1[tok[c]], ob, atol=1e-12)
