@@ -429,7 +429,7 @@ def main():
                     "vsa_fine_fixed_first_over_guarded": pk["wf_vsa_fine_fixed_first"] / pk["wf_vsa_fine"]}
 
     # extra record (not part of the step): sliding-tile attention on the two tuned grids, 40 heads,
-    # 5x5x5-cube windows (own inputs; the step's tensors are unchanged)
+    # 3x3x3 windows of 6x8x8-token tiles (own inputs; the step's tensors are unchanged)
     sta = None
     if not args.no_extra:
         sta = {}
@@ -447,20 +447,22 @@ def main():
                 wf.wf_sta(qs_, ks2, vs2, gs, ws_.window, out=os2, workspace=wsb)
             torch.cuda.synchronize()
             sk2 = {}
-            for kname in ("wf_vsa_gather", "wf_sta_plan", "wf_sta_fine"):
+            for kname in ("wf_sta_gather", "wf_sta_plan", "wf_sta_fine"):
                 n, tot = wf.profile_query(kname)
                 sk2[kname] = tot / n
             wf.profile_enable(False)
             kk = ws_.window[0] * ws_.window[1] * ws_.window[2]
-            cubes = wf.num_cubes(*gs)
-            fine_fl = 4.0 * ws_.B * ws_.Hh * ws_.N * 64 * kk * ws_.D
+            tiles = (ws_.T // 6) * (ws_.H // 8) * (ws_.W // 8)
+            fine_fl = 4.0 * ws_.B * ws_.Hh * ws_.N * 384 * kk * ws_.D   # every query against 384 kk keys
             ms = sum(sk2.values())
             dense_ms = dense_flops(ws_) / (dense_tf_step * 1e12) * 1e3  # dense at this shape, at the step's rate
-            sta[name] = {"grid": list(gs), "heads": ws_.Hh, "cubes": cubes, "window": list(ws_.window),
-                         "key_cubes_per_query_cube": kk, "ms_per_call": ms, "kernel_ms": sk2,
+            sta[name] = {"grid": list(gs), "heads": ws_.Hh, "tiles": tiles, "tile": [6, 8, 8],
+                         "window_tiles": list(ws_.window), "key_tiles_per_query_tile": kk,
+                         "density": kk / tiles, "ms_per_call": ms, "kernel_ms": sk2,
                          "fine_tflops": fine_fl / (sk2["wf_sta_fine"] * 1e-3) / 1e12,
                          "dense_equivalent_ms_at_step_rate": dense_ms,
-                         "dense_equivalent_speedup": dense_ms / ms}
+                         "dense_equivalent_speedup": dense_ms / ms,
+                         "ideal_speedup": tiles / kk}
             del qs_, ks2, vs2, os2, wsb
 
     # extra record (not part of the step): the 720p shape -- dense attention on the CFG pair at

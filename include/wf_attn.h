@@ -145,10 +145,15 @@ int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v,
  *   workspace      as filled by wf_vsa_coarse_topk with the same B, Hh, T, H, W, D.
  *   idx            int32 [B][Hh][C][topk]: any plan (the coarse stage's or the
  *                  caller's) with entries in [0, C) strictly ascending per row.
- *                  The kernels trust it unless the environment variable
- *                  WF_VALIDATE=1 is set, in which case a check kernel runs
- *                  first and the call synchronises `stream` to return
- *                  WF_ERR_BAD_INDEX on a bad plan (nothing else enqueued).
+ *                  Without a check the kernels take it as given, but they
+ *                  never read outside the workspace whatever it holds: every
+ *                  key-cube copy is range-checked against the head's C cubes,
+ *                  and an entry outside [0, C) reads zero keys and values (the
+ *                  rows of that query cube are then meaningless, not a
+ *                  fault).  With the environment variable WF_VALIDATE=1 a
+ *                  check kernel runs first and the call synchronises `stream`
+ *                  to return WF_ERR_BAD_INDEX on a bad plan (nothing else
+ *                  enqueued).
  *   o              fp32 [B][Hh][T*H*W][D] in grid order, written.
  *   lse            fp32 [B][Hh][T*H*W], written; may be NULL.
  */
@@ -188,23 +193,29 @@ int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t
 
 /*
  * Sliding-tile attention (STA).  "推理优化" (Inference optimization,
- * WorldFoundry docs), approximate-attention section, entry "sta", lists
- * weight-free sliding-tile attention for the Wan DiT on its tuned token grids
- * (36, 48, 48) and (18, 48, 80), without tile or window sizes.  The library's
- * definition, on VSA's cube layout (any grid VSA accepts):
- *   - tiles are the 4x4x4 cubes of the padded grid (padded slots masked);
- *   - query cube c attends to the cubes of a wt x wh x ww-cube window that on
+ * WorldFoundry docs), approximate-attention section, entry "sta": weight-free
+ * sliding-tile attention for the Wan DiT, accepted only on its tuned token
+ * grids (36, 48, 48) and (18, 48, 80) and refused, before any GPU work, on any
+ * other (the page's example is the default (31, 22, 40)).  It gives no tile or
+ * window size; the library's definition:
+ *   - tiles are 6 x 8 x 8 tokens (t, h, w), which both accepted grids divide
+ *     exactly (6x6x6 and 3x6x10 tiles; no padding), tile id (tt*nh + th)*nw + tw;
+ *   - a query tile attends to the tiles of a wt x wh x ww-tile window that on
  *     each axis starts at clamp(c - (w-1)/2, 0, n - w): centred where it fits,
- *     pushed inward at the grid's edge, so every cube sees wt*wh*ww cubes;
- *   - each real query token attends to every real key token of those cubes:
+ *     pushed inward at the grid's edge, so every tile sees wt*wh*ww tiles;
+ *   - each query token attends to every key token of those tiles:
  *     o[i] = sum_j softmax_j(scale * q[i] . k[j]) v[j], lse as in wf_vsa_fine.
- * This is wf_vsa_fine with a fixed plan instead of a top-k one.
+ * The kernels run it as VSA's fine stage over 1x8x8-token slabs with a fixed
+ * plan (six slabs per tile).
  *
+ *   T, H, W     36 x 48 x 48 or 18 x 48 x 80, else WF_ERR_UNSUPPORTED.
  *   q, k, v     bf16 [B][Hh][T*H*W][D]; D must be 128.
- *   wt, wh, ww  window in cubes, 1 <= w <= ceil(axis/4).
+ *   wt, wh, ww  window in tiles, 1 <= wt <= T/6, 1 <= wh <= H/8, 1 <= ww <= W/8.
  *   o           fp32 [B][Hh][T*H*W][D], written; lse fp32 [B][Hh][T*H*W] or NULL.
- *   plan        int32 [C][wt*wh*ww], written (ascending rows); may be NULL.
- *   workspace   at least wf_sta_workspace_bytes() bytes.
+ *   plan        int32 [T/6 * H/8 * W/8][wt*wh*ww], the key tiles of every
+ *               query tile, written (ascending rows); may be NULL.
+ *   workspace   at least wf_sta_workspace_bytes() bytes (0 for a grid or
+ *               window the call would refuse).
  */
 size_t wf_sta_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D,
                               int32_t wt, int32_t wh, int32_t ww);

@@ -85,11 +85,11 @@ WORKLOADS = {
     # the page's operating point: 78 of 624 cubes (87.5% sparsity)
     "vsa_480p_k78": Workload("vsa_480p_k78", 1, 40, 21, 30, 52, 128, True, 4, topk=78,
                              note="VSA, 480p grid, 624 cubes, top-78 (the review's 87.5% sparsity)"),
-    # sliding-tile attention on its two tuned token grids, 5x5x5-cube windows
-    "sta_36x48x48": Workload("sta_36x48x48", 1, 40, 36, 48, 48, 128, True, 6, window=(5, 5, 5),
-                             note="STA, grid 36x48x48 (1,296 cubes), window 5x5x5 cubes"),
-    "sta_18x48x80": Workload("sta_18x48x80", 1, 40, 18, 48, 80, 128, True, 7, window=(5, 5, 5),
-                             note="STA, grid 18x48x80 padded to 20x48x80 (1,200 cubes), window 5x5x5 cubes"),
+    # sliding-tile attention on its two tuned token grids, 3x3x3-tile windows of 6x8x8-token tiles
+    "sta_36x48x48": Workload("sta_36x48x48", 1, 40, 36, 48, 48, 128, True, 6, window=(3, 3, 3),
+                             note="STA, grid 36x48x48 (6x6x6 tiles of 6x8x8), window 3x3x3 tiles"),
+    "sta_18x48x80": Workload("sta_18x48x80", 1, 40, 18, 48, 80, 128, True, 7, window=(3, 3, 3),
+                             note="STA, grid 18x48x80 (3x6x10 tiles of 6x8x8), window 3x3x3 tiles"),
 }
 
 

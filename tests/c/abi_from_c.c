@@ -42,7 +42,9 @@ int main(void) {
   EXPECT(wf_vsa_fine(fake, 16, (const int32_t*)fake, 1, 2, 5, 6, 7, 128, 0.1f, 2, (float*)fake, NULL, NULL) ==
          WF_ERR_WORKSPACE);
   EXPECT(wf_rope_qk(fake, fake, fake, fake, 1, 2, 5, 6, 7, 128, 1e4, 16, NULL) == WF_ERR_INVALID_ARG);
-  EXPECT(wf_sta(fake, fake, fake, 1, 2, 5, 6, 7, 128, 0.1f, 3, 1, 1, (float*)fake, NULL, NULL, fake, 1u << 30,
+  EXPECT(wf_sta(fake, fake, fake, 1, 2, 5, 6, 7, 128, 0.1f, 1, 1, 1, (float*)fake, NULL, NULL, fake, 1u << 30,
+                NULL) == WF_ERR_UNSUPPORTED);
+  EXPECT(wf_sta(fake, fake, fake, 1, 2, 18, 48, 80, 128, 0.1f, 4, 1, 1, (float*)fake, NULL, NULL, fake, 1u << 30,
                 NULL) == WF_ERR_INVALID_ARG);
   {
     int64_t n = 0;

@@ -137,13 +137,19 @@ def test_vsa_argument_errors(wf):
     assert fex(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 7, FAKE, None, None) == 1
     assert fex(FAKE, 10, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 2, FAKE, None, None) == 3
     sta = wf.lib.wf_sta
-    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1
-    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 0, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1
-    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 64, 0.1, 1, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 2
-    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 2, 2, 2, FAKE, None, None, FAKE, 10, None) == 3
-    assert sta(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 2, 2, 2, FAKE, None, FAKE + 2, FAKE, 1 << 30, None) == 1
-    assert wf.lib.wf_sta_workspace_bytes(1, 2, 5, 6, 7, 128, 3, 1, 1) == 0
-    assert wf.lib.wf_sta_workspace_bytes(1, 40, 36, 48, 48, 128, 5, 5, 5) > 0
+    G = (18, 48, 80)                                       # a tuned grid: 3 x 6 x 10 tiles of 6x8x8
+    assert sta(FAKE, FAKE, FAKE, 1, 2, *G, 128, 0.1, 4, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    assert sta(FAKE, FAKE, FAKE, 1, 2, *G, 128, 0.1, 1, 7, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    assert sta(FAKE, FAKE, FAKE, 1, 2, *G, 128, 0.1, 0, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    assert sta(FAKE, FAKE, FAKE, 1, 2, *G, 64, 0.1, 1, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 2
+    assert sta(FAKE, FAKE, FAKE, 1, 2, *G, 128, 0.1, 2, 2, 2, FAKE, None, None, FAKE, 10, None) == 3
+    assert sta(FAKE, FAKE, FAKE, 1, 2, *G, 128, 0.1, 2, 2, 2, FAKE, None, FAKE + 2, FAKE, 1 << 30, None) == 1
+    for grid in ((5, 6, 7), (31, 22, 40), (36, 48, 40), (24, 48, 48)):   # not tuned: refused, no GPU work
+        assert sta(FAKE, FAKE, FAKE, 1, 2, *grid, 128, 0.1, 1, 1, 1, FAKE, None, None, FAKE, 1 << 30, None) == 2
+        assert b"tuned grids" in wf.lib.wf_last_error_detail()
+        assert wf.lib.wf_sta_workspace_bytes(1, 2, *grid, 128, 1, 1, 1) == 0
+    assert wf.lib.wf_sta_workspace_bytes(1, 40, 36, 48, 48, 128, 3, 3, 3) > 0
+    assert wf.lib.wf_sta_workspace_bytes(1, 40, 36, 48, 48, 128, 7, 1, 1) == 0
     gated = wf.lib.wf_vsa_fine_gated
     assert gated(FAKE, 1 << 30, FAKE, None, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1
     assert gated(FAKE, 1 << 30, FAKE, FAKE + 4, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None) == 1

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 GRID = (9, 10, 11)  # 990 tokens, padded to 12 x 12 x 12: 27 cubes, ragged in every axis
 TOPK = 4
-WINDOW = (3, 3, 3)
+STA_GRID = (18, 48, 80)  # sliding-tile attention runs on its tuned grids only (3 x 6 x 10 tiles)
+WINDOW = (1, 2, 3)
 
 
 @pytest.fixture(scope="module")
@@ -34,7 +35,8 @@ def wf():
 def inputs(seed):
     wl = synth.small_workload("graph", 1, 3, *GRID, 128, structured=True, seed=seed, topk=TOPK)
     q, k, v = (to_device(x) for x in synth.make_qkv(wl))
-    return q, k, v, to_device(synth.make_gate(wl))
+    ws = synth.small_workload("graph_sta", 1, 1, *STA_GRID, 128, structured=True, seed=seed + 50)
+    return q, k, v, to_device(synth.make_gate(wl)), tuple(to_device(x) for x in synth.make_qkv(ws))
 
 
 def buffers(wf, q):
@@ -44,7 +46,8 @@ def buffers(wf, q):
     T, H, W = GRID
     C = wf.num_cubes(T, H, W)
     f32 = dict(dtype=torch.float32, device=q.device)
-    ws_sta = wf.lib.wf_sta_workspace_bytes(B, Hh, T, H, W, D, *WINDOW)
+    ws_sta = wf.lib.wf_sta_workspace_bytes(1, 1, *STA_GRID, D, *WINDOW)
+    Ns = STA_GRID[0] * STA_GRID[1] * STA_GRID[2]
     return dict(
         o_dense=torch.empty((B, Hh, N, D), **f32), lse_dense=torch.empty((B, Hh, N), **f32),
         q_rot=torch.empty_like(q), k_rot=torch.empty_like(q),
@@ -52,7 +55,7 @@ def buffers(wf, q):
         scores=torch.empty((B, Hh, C, C), **f32),
         o_fine=torch.empty((B, Hh, N, D), **f32), lse_fine=torch.empty((B, Hh, N), **f32),
         o_gated=torch.empty((B, Hh, N, D), **f32), o_coarse=torch.empty((B, Hh, C, D), **f32),
-        o_sta=torch.empty((B, Hh, N, D), **f32),
+        o_sta=torch.empty((1, 1, Ns, D), **f32),
         ws_dense=torch.empty(wf.dense_workspace_bytes(B, Hh, N, D), dtype=torch.uint8, device=q.device),
         ws_vsa=torch.empty(wf.vsa_workspace_bytes(B, Hh, T, H, W, D), dtype=torch.uint8, device=q.device),
         ws_sta=torch.empty(ws_sta, dtype=torch.uint8, device=q.device),
@@ -63,7 +66,7 @@ OUTPUTS = ("o_dense", "lse_dense", "q_rot", "k_rot", "idx", "scores", "o_fine", 
            "o_coarse", "o_sta")
 
 
-def path(wf, q, k, v, gate, b):
+def path(wf, q, k, v, gate, sta_qkv, b):
     """The whole path once: dense, RoPE, VSA coarse (RoPE fused) + fine + gated, STA."""
     wf.wf_attn_dense(q, k, v, out=b["o_dense"], lse=b["lse_dense"], workspace=b["ws_dense"])
     wf.wf_rope_qk(q, k, GRID, q_out=b["q_rot"], k_out=b["k_rot"])
@@ -71,7 +74,7 @@ def path(wf, q, k, v, gate, b):
                           rope_theta=10000.0)
     wf.wf_vsa_fine(b["ws_vsa"], b["idx"], tuple(q.shape), GRID, out=b["o_fine"], lse=b["lse_fine"])
     wf.wf_vsa_fine_gated(b["ws_vsa"], b["idx"], gate, GRID, out=b["o_gated"], o_coarse=b["o_coarse"])
-    wf.wf_sta(q, k, v, GRID, WINDOW, out=b["o_sta"], lse=None, workspace=b["ws_sta"])
+    wf.wf_sta(*sta_qkv, STA_GRID, WINDOW, out=b["o_sta"], lse=None, workspace=b["ws_sta"])
 
 
 def poison(b):
@@ -83,11 +86,11 @@ def poison(b):
             t.fill_(-1)
 
 
-def eager(wf, q, k, v, gate):
+def eager(wf, q, k, v, gate, sta_qkv):
     import torch
     b = buffers(wf, q)
     poison(b)
-    path(wf, q, k, v, gate, b)
+    path(wf, q, k, v, gate, sta_qkv, b)
     torch.cuda.synchronize()
     return {name: b[name].clone() for name in OUTPUTS}
 
@@ -104,14 +107,14 @@ def assert_same(got, want, when):
 def test_graph_replays_match_eager(wf):
     import torch
     log("graph capture: eager reference")
-    q, k, v, gate = inputs(seed=901)
-    want = eager(wf, q, k, v, gate)
+    q, k, v, gate, sq = inputs(seed=901)
+    want = eager(wf, q, k, v, gate, sq)
 
     log("graph capture: capture the path")
     b = buffers(wf, q)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        path(wf, q, k, v, gate, b)
+        path(wf, q, k, v, gate, sq, b)
     torch.cuda.synchronize()
 
     x = torch.randn(512, 512, device=q.device)
@@ -126,10 +129,11 @@ def test_graph_replays_match_eager(wf):
         assert_same(b, want, f"replay {r}")
 
     log("graph capture: new input contents, replay")
-    q2, k2, v2, gate2 = inputs(seed=902)
-    want2 = eager(wf, q2, k2, v2, gate2)
+    q2, k2, v2, gate2, sq2 = inputs(seed=902)
+    want2 = eager(wf, q2, k2, v2, gate2, sq2)
     assert not torch.equal(want2["o_dense"], want["o_dense"])
-    for dst, src in ((q, q2), (k, k2), (v, v2), (gate, gate2)):
+    assert not torch.equal(want2["o_sta"], want["o_sta"])
+    for dst, src in ((q, q2), (k, k2), (v, v2), (gate, gate2)) + tuple(zip(sq, sq2)):
         dst.copy_(src)
     poison(b)
     torch.cuda.synchronize()

@@ -296,9 +296,10 @@ def wf_vsa_fine_gated(workspace, idx, gate, grid, scale: Optional[float] = None,
 
 def wf_sta(q, k, v, grid, window, scale: Optional[float] = None, with_lse: bool = False,
            with_plan: bool = False, out=None, lse=None, workspace=None):
-    """Sliding-tile attention through wf_sta.  window = (wt, wh, ww) in cubes.
+    """Sliding-tile attention through wf_sta.  window = (wt, wh, ww) in 6x8x8-token tiles; grid is
+    one of the two tuned grids (36, 48, 48) and (18, 48, 80) (the library refuses any other).
 
-    Returns (o, lse or None, plan int32 [C, wt*wh*ww] or None).
+    Returns (o, lse or None, plan int32 [tiles, wt*wh*ww] or None).
     """
     torch = _torch()
     _qkv_check(q, k, v)
@@ -312,7 +313,8 @@ def wf_sta(q, k, v, grid, window, scale: Optional[float] = None, with_lse: bool 
         out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=q.device)
     if with_lse and lse is None:
         lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
-    plan = (torch.empty((num_cubes(T, H, W), wt * wh * ww), dtype=torch.int32, device=q.device)
+    tiles = (T // 6) * (H // 8) * (W // 8)
+    plan = (torch.empty((max(tiles, 1), wt * wh * ww), dtype=torch.int32, device=q.device)
             if with_plan else None)
     _expect(out, "out", (B, Hh, N, D), torch.float32, q.device)
     _expect(lse, "lse", (B, Hh, N), torch.float32, q.device)

@@ -351,13 +351,25 @@ int32_t wf_vsa_fine_gated(void* workspace, size_t workspace_bytes, const int32_t
   return ok();
 }
 
+// Sliding-tile attention runs on the two token grids it is tuned for and refuses every other
+// grid before any GPU work ("推理优化", approximate attention, entry "sta").  Both are whole
+// numbers of 6x8x8 tiles.
+static bool sta_tuned_grid(int32_t T, int32_t H, int32_t W) {
+  return (T == 36 && H == 48 && W == 48) || (T == 18 && H == 48 && W == 80);
+}
+
 static int32_t sta_check(int32_t B, int32_t Hh, int32_t T, int32_t H, int32_t W, int32_t D, int32_t wt,
                          int32_t wh, int32_t ww) {
+  if (!sta_tuned_grid(T, H, W))
+    return fail(WF_ERR_UNSUPPORTED, "sliding-tile attention runs on the tuned grids 36x48x48 and 18x48x80 only, "
+                "not %dx%dx%d", T, H, W);
   if (int32_t st = vsa_check_sizes(B, Hh, T, H, W, D)) return st;
-  const int nt = (T + 3) / 4, nh = (H + 3) / 4, nw = (W + 3) / 4;
+  const int nt = T / 6, nh = H / 8, nw = W / 8;
   if (wt < 1 || wt > nt || wh < 1 || wh > nh || ww < 1 || ww > nw)
-    return fail(WF_ERR_INVALID_ARG, "window %dx%dx%d cubes must fit the cube grid %dx%dx%d", wt, wh, ww, nt, nh,
+    return fail(WF_ERR_INVALID_ARG, "window %dx%dx%d tiles must fit the tile grid %dx%dx%d", wt, wh, ww, nt, nh,
                 nw);
+  if ((long long)B * Hh * wf::sta_slabs(T, H, W) >= (1ll << 31))
+    return fail(WF_ERR_UNSUPPORTED, "B=%d Hh=%d: too many workgroups for one launch", B, Hh);
   return WF_OK;
 }
 

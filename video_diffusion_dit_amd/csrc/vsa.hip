@@ -18,14 +18,28 @@ static_assert(kSoftmaxGuarded == WF_SOFTMAX_GUARDED && kSoftmaxRunningMax == WF_
                   kSoftmaxFixedFirst == WF_SOFTMAX_FIXED_FIRST_TILE,
               "softmax policy numbers of the C ABI and the kernels");
 
-// Cs: the cube count rounded up to a multiple of 32, the row stride of the
-// coarse scores and of the transposed cube means of V in the workspace.
+// Blocks of 64 tokens the gather and the fine stage work on: VSA's 4x4x4 cubes
+// ("VSA selects cubes"), and 1x8x8 slabs for sliding-tile attention, whose
+// 6x8x8 tiles are six slabs stacked along t.  Slot s of a block is row-major:
+// (s / (BH*BW), s / BW % BH, s % BW).
+template <int BT_, int BH_, int BW_>
+struct Block {
+  static constexpr int BT = BT_, BH = BH_, BW = BW_;
+  static_assert(BT * BH * BW == 64, "a block is 64 tokens");
+};
+using Cube = Block<4, 4, 4>;
+using Slab = Block<1, 8, 8>;
+
+// The block grid of a T x H x W token grid (each axis padded up to a whole
+// number of blocks).  Cs: the block count rounded up to a multiple of 32, the
+// row stride of the coarse scores and of the transposed cube means of V.
 struct Grid3 {
   int T, H, W, nt, nh, nw, C, Cs;
 };
 
+template <class BLK>
 static Grid3 make_grid(int T, int H, int W) {
-  Grid3 g{T, H, W, (T + 3) / 4, (H + 3) / 4, (W + 3) / 4, 0, 0};
+  Grid3 g{T, H, W, (T + BLK::BT - 1) / BLK::BT, (H + BLK::BH - 1) / BLK::BH, (W + BLK::BW - 1) / BLK::BW, 0, 0};
   g.C = g.nt * g.nh * g.nw;
   g.Cs = (g.C + 31) / 32 * 32;
   return g;
@@ -42,9 +56,11 @@ __device__ __forceinline__ long vbar_index(int part, int bh, int BH, int Cs, int
   return ((((long)part * BH + bh) * (Cs / 16) + key / 16) * 4 + d / 32) * 512 + lane * 8 + key % 8;
 }
 
-// Token of slot s in cube (ct, ch, cw), or -1 for a padded slot.
+// Token of slot s in block (ct, ch, cw), or -1 for a padded slot.
+template <class BLK>
 __device__ __forceinline__ int slot_token(const Grid3& g, int ct, int ch, int cw, int s) {
-  const int t = ct * 4 + (s >> 4), h = ch * 4 + ((s >> 2) & 3), w = cw * 4 + (s & 3);
+  const int t = ct * BLK::BT + s / (BLK::BH * BLK::BW), h = ch * BLK::BH + (s / BLK::BW) % BLK::BH,
+            w = cw * BLK::BW + s % BLK::BW;
   return (t < g.T && h < g.H && w < g.W) ? (t * g.H + h) * g.W + w : -1;
 }
 
@@ -55,30 +71,32 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 }
 
 // ---------------------------------------------------------------- gather + pool
-// One workgroup per (bh, cube).  Writes Qc, Kc [BH][C][64][D] (padded slots
-// zero), Vct [BH][C][D][64] (slots in perm16 order), the fp32 means of Q and K
-// over the cube's real tokens, and the fp32 mean of V split into two bf16
-// parts, hi = bf16(mean) and lo = bf16(mean - hi), at key cube c of the
-// operand-ordered means (vbar_index; key cubes C..Cs-1 are zeroed, so the
-// coarse-branch product may run over whole 32-wide steps).  With ROPE, Q and
-// K are rotated by the 3D RoPE (wf_rope.hpp) on the way in, so everything
+// One workgroup per (bh, block).  Writes Qc, Kc [BH][C][64][D] (padded slots
+// zero), Vct [BH][C][D][64] (slots in perm16 order) and, with POOL, the fp32
+// means of Q and K over the block's real tokens, and the fp32 mean of V split
+// into two bf16 parts, hi = bf16(mean) and lo = bf16(mean - hi), at key cube c
+// of the operand-ordered means (vbar_index; key cubes C..Cs-1 are zeroed, so
+// the coarse-branch product may run over whole 32-wide steps).  With ROPE, Q
+// and K are rotated by the 3D RoPE (wf_rope.hpp) on the way in, so everything
 // downstream (cube means, scores, the fine stage) sees the rotated vectors;
 // the cube's 4 t, 4 h and 4 w coordinates need one table of 4*(t2+h2+w2)
 // (cos, sin) pairs, one fp64 sincos per thread.  ROPE is the rotation's
-// precision (32 or 64), 0 for none.
-template <int D, int ROPE>
+// precision (32 or 64), 0 for none.  BLK is the block shape (VSA's cubes, or
+// sliding-tile attention's slabs, which need no means).
+template <int D, int ROPE, class BLK = Cube, bool POOL = true>
 __global__ void __launch_bounds__(256) wf_vsa_gather(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ qc, uint16_t* __restrict__ kc, uint16_t* __restrict__ vct,
     float* __restrict__ qbar, float* __restrict__ kbar, uint16_t* __restrict__ vbt, Grid3 g,
     double theta) {
+  static_assert(ROPE == 0 || (BLK::BT == 4 && BLK::BH == 4 && BLK::BW == 4), "RoPE is fused for cubes only");
   constexpr int ROWCH = D / 8;            // 16-byte chunks per row
   constexpr int RSTEP = 256 / ROWCH;      // rows covered by one pass of the workgroup
   constexpr int VSTR = D + 2;
   constexpr RopeSplit sp = rope_split(D);
   constexpr int NTAB = ROPE ? 4 * (sp.t2 + sp.h2 + sp.w2) : 1;
   using CS = RopeCS<ROPE == 64 ? 64 : 32>;
-  __shared__ float red[RSTEP][D];
+  __shared__ float red[POOL ? RSTEP : 1][D];
   __shared__ uint16_t vtile[64 * VSTR];
   __shared__ CS tab[NTAB];
   const int tid = threadIdx.x, c16 = tid % ROWCH, r0 = tid / ROWCH;
@@ -100,7 +118,8 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
   }
   const long N = (long)g.T * g.H * g.W;
   const long cube_row0 = ((long)bh * g.C + c) * 64;
-  const int count = min(4, g.T - 4 * ct) * min(4, g.H - 4 * ch) * min(4, g.W - 4 * cw);
+  const int count = min(BLK::BT, g.T - BLK::BT * ct) * min(BLK::BH, g.H - BLK::BH * ch) *
+                    min(BLK::BW, g.W - BLK::BW * cw);
 
   for (int which = 0; which < 3; ++which) {
     const uint16_t* src = (which == 0 ? q : which == 1 ? k : v) + (long)bh * N * D;
@@ -108,7 +127,7 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
 #pragma unroll
     for (int i = 0; i < 64 / RSTEP; ++i) {
       const int s = r0 + i * RSTEP;
-      const int tok = slot_token(g, ct, ch, cw, s);
+      const int tok = slot_token<BLK>(g, ct, ch, cw, s);
       uint4 u = make_uint4(0, 0, 0, 0);
       if (tok >= 0) u = *reinterpret_cast<const uint4*>(src + (long)tok * D + c16 * 8);
       if constexpr (ROPE != 0) {
@@ -129,27 +148,31 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
 #pragma unroll
         for (int t = 0; t < 8; ++t) vtile[s * VSTR + c16 * 8 + t] = e[t];
       }
+      if constexpr (POOL) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] += __uint_as_float((uint32_t)e[t] << 16);
+        for (int t = 0; t < 8; ++t) acc[t] += __uint_as_float((uint32_t)e[t] << 16);
+      }
     }
+    if constexpr (POOL) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) red[r0][c16 * 8 + t] = acc[t];
-    __syncthreads();
-    if (tid < D) {
-      float sum = 0.f;
+      for (int t = 0; t < 8; ++t) red[r0][c16 * 8 + t] = acc[t];
+      __syncthreads();
+      if (tid < D) {
+        float sum = 0.f;
 #pragma unroll
-      for (int r = 0; r < RSTEP; ++r) sum += red[r][tid];
-      const float mean = sum / (float)count;
-      if (which < 2) {
-        (which == 0 ? qbar : kbar)[((long)bh * g.C + c) * D + tid] = mean;
-      } else {
-        static_assert(D == 128, "four 32-wide head-dim blocks");
-        const int BH = gridDim.x / g.C;  // gridDim.x = BH * C
-        const __bf16 h16 = (__bf16)mean;
-        vbt[vbar_index(0, bh, BH, g.Cs, c, tid)] = __builtin_bit_cast(uint16_t, h16);
-        vbt[vbar_index(1, bh, BH, g.Cs, c, tid)] = __builtin_bit_cast(uint16_t, (__bf16)(mean - (float)h16));
-        for (int x = g.C + c; x < g.Cs; x += g.C)
-          vbt[vbar_index(0, bh, BH, g.Cs, x, tid)] = vbt[vbar_index(1, bh, BH, g.Cs, x, tid)] = 0;
+        for (int r = 0; r < RSTEP; ++r) sum += red[r][tid];
+        const float mean = sum / (float)count;
+        if (which < 2) {
+          (which == 0 ? qbar : kbar)[((long)bh * g.C + c) * D + tid] = mean;
+        } else {
+          static_assert(D == 128, "four 32-wide head-dim blocks");
+          const int BH = gridDim.x / g.C;  // gridDim.x = BH * C
+          const __bf16 h16 = (__bf16)mean;
+          vbt[vbar_index(0, bh, BH, g.Cs, c, tid)] = __builtin_bit_cast(uint16_t, h16);
+          vbt[vbar_index(1, bh, BH, g.Cs, c, tid)] = __builtin_bit_cast(uint16_t, (__bf16)(mean - (float)h16));
+          for (int x = g.C + c; x < g.Cs; x += g.C)
+            vbt[vbar_index(0, bh, BH, g.Cs, x, tid)] = vbt[vbar_index(1, bh, BH, g.Cs, x, tid)] = 0;
+        }
       }
     }
     __syncthreads();
@@ -407,7 +430,7 @@ __global__ void __launch_bounds__(256) wf_vsa_coarse_out(const float* __restrict
 // writes and the row reads free of bank conflicts.  With GATED the merge
 // O = O_fine + gate * Oc is applied on the way out, where the gate is read
 // row-contiguously as well.
-template <int D, bool GATED>
+template <int D, bool GATED, class BLK>
 __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* slot_lds, int j, int half,
                                               const Grid3& g, int ct, int ch, int cw, int wave, long head_row0,
                                               float* __restrict__ out, const uint16_t* __restrict__ gate,
@@ -428,7 +451,7 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
 #pragma unroll 4
   for (int i = 0; i < 16; ++i) {
     const int r = 2 * i + lane / 32;  // row inside this wavefront's 32
-    const int tok = slot_token(g, ct, ch, cw, wave * 32 + r);
+    const int tok = slot_token<BLK>(g, ct, ch, cw, wave * 32 + r);
     float4 v = *reinterpret_cast<const float4*>(lds + r * D + ((c ^ r) * 4));
     if (tok >= 0) {
       const long row = head_row0 + tok;
@@ -457,8 +480,9 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
 // softmax.  Padded key slots of edge cubes are masked; output rows are
 // scattered back to grid order, padded query slots are not written.  With
 // GATED the epilogue adds gate * Oc of the query cube (gated merge).  SM
-// selects the softmax reference policy (softmax_tile).
-template <int D, bool GATED, int SM = kSoftmaxGuarded>
+// selects the softmax reference policy (softmax_tile).  BLK is the shape of
+// the 64-token blocks (VSA's cubes; sliding-tile attention's slabs).
+template <int D, bool GATED, int SM = kSoftmaxGuarded, class BLK = Cube>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vct, const int* __restrict__ idx, float* __restrict__ o,
@@ -492,26 +516,30 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
 
   int cur = plan[0];
   const CopyOffsets<D, 2> coff(wave, lane, 64);
-  constexpr uint32_t CUBE_BYTES = 64u * D * 2;
   constexpr int KP = CopyOffsets<D, 2>::KPW, VP = CopyOffsets<D, 2>::VPW;  // copies per wavefront and tile
-  tile_copy<D, 2>(coff, kc + (cube_base + cur) * 64 * D, 64, ks, nullptr, 0, 0, nullptr, wave);
-  tile_copy<D, 2>(coff, nullptr, 0, nullptr, vct + (cube_base + cur) * D * 64, 64, CUBE_BYTES, vs, wave);
+  // the head's cube-ordered K and V^T: every copy is range-checked against these C cubes, so a
+  // plan entry outside [0, C) reads zeros (cube_copy) instead of memory beyond them
+  const uint16_t* khead = kc + cube_base * 64 * D;
+  const uint16_t* vhead = vct + cube_base * D * 64;
+  cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, cur, g.C, wave);
+  cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cur, g.C, wave);
   wait_tile_copies_keep<VP>();  // K(0) landed; V(0) may still fly
   for (int t = 0; t < k; ++t) {
     barrier_nofence();  // K(t) visible
     mfma_run<D, NPV, NPV + NQK>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
     barrier_nofence();                                                     // K slot free
     const int nxt = t + 1 < k ? plan[t + 1] : cur;  // past the end: a harmless copy of the last cube
-    tile_copy<D, 2>(coff, kc + (cube_base + nxt) * 64 * D, 64, ks, nullptr, 0, 0, nullptr, wave);
+    cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, nxt, g.C, wave);
     int kt, kh, kw;
     cube_coords(g, cur, kt, kh, kw);
-    const int lt = g.T - 4 * kt, lh = g.H - 4 * kh, lw = g.W - 4 * kw;
-    if (lt < 4 || lh < 4 || lw < 4) {  // edge cube: mask padded key slots
+    const int lt = g.T - BLK::BT * kt, lh = g.H - BLK::BH * kh, lw = g.W - BLK::BW * kw;
+    if (lt < BLK::BT || lh < BLK::BH || lw < BLK::BW) {  // edge block: mask padded key slots
+      constexpr int PL = BLK::BH * BLK::BW;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int a = key_row(0, r, half), b = key_row(1, r, half);
-        if (!((a >> 4) < lt && ((a >> 2) & 3) < lh && (a & 3) < lw)) s0[r] = -INFINITY;
-        if (!((b >> 4) < lt && ((b >> 2) & 3) < lh && (b & 3) < lw)) s1[r] = -INFINITY;
+        if (!(a / PL < lt && (a / BLK::BW) % BLK::BH < lh && a % BLK::BW < lw)) s0[r] = -INFINITY;
+        if (!(b / PL < lt && (b / BLK::BW) % BLK::BH < lh && b % BLK::BW < lw)) s1[r] = -INFINITY;
       }
     }
     softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, p2);
@@ -519,7 +547,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     barrier_nofence();            // V(t) visible
     mfma_run<D, 0, NPV>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // O += P V(t)
     barrier_nofence();                                             // V slot free
-    tile_copy<D, 2>(coff, nullptr, 0, nullptr, vct + (cube_base + nxt) * D * 64, 64, CUBE_BYTES, vs, wave);
+    cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, nxt, g.C, wave);
     wait_tile_copies_keep<VP>();  // K(t+1) landed; V(t+1) may fly
     cur = nxt;
   }
@@ -529,32 +557,48 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   cube_coords(g, c, ct, ch, cw);
   const long head_row0 = (long)bh * g.T * g.H * g.W;
   const float lt = l + __shfl_xor(l, 32);
-  fine_epilogue<D, GATED>(oacc, 1.f / lt, wave == 0 ? ks : vs, j, half, g, ct, ch, cw, wave, head_row0, o,
-                          gate, GATED ? ocoarse + (cube_base + c) * D : nullptr);
-  const int tok = slot_token(g, ct, ch, cw, slot);
+  fine_epilogue<D, GATED, BLK>(oacc, 1.f / lt, wave == 0 ? ks : vs, j, half, g, ct, ch, cw, wave, head_row0, o,
+                               gate, GATED ? ocoarse + (cube_base + c) * D : nullptr);
+  const int tok = slot_token<BLK>(g, ct, ch, cw, slot);
   if (lse && tok >= 0 && half == 0) lse[head_row0 + tok] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------- sliding-tile plan
 // Sliding-tile attention ("推理优化", WorldFoundry docs, approximate attention,
-// entry "sta": weight-free, on tuned grids; tile and window sizes are not
-// given there): query cube c attends to the cubes of a (wt, wh, ww)-cube
-// window, on each axis starting at clamp(c - (w-1)/2, 0, n - w) -- centred
-// where it fits, pushed inward at the edges -- so every row has wt*wh*ww
-// cubes.  One thread per (cube, slot); slots run row-major over the window,
-// which lists the cubes in ascending order.
-__global__ void __launch_bounds__(256) wf_sta_plan(int* __restrict__ plan, Grid3 g, int wt, int wh, int ww) {
-  const int k = wt * wh * ww;
-  const long id = (long)blockIdx.x * 256 + threadIdx.x;
-  if (id >= (long)g.C * k) return;
-  const int c = (int)(id / k), j = (int)(id % k);
-  int ct, ch, cw;
-  cube_coords(g, c, ct, ch, cw);
-  const int t0 = min(max(ct - (wt - 1) / 2, 0), g.nt - wt);
-  const int h0 = min(max(ch - (wh - 1) / 2, 0), g.nh - wh);
-  const int w0 = min(max(cw - (ww - 1) / 2, 0), g.nw - ww);
-  const int jt = j / (wh * ww), jh = (j / ww) % wh, jw = j % ww;
-  plan[id] = ((t0 + jt) * g.nh + (h0 + jh)) * g.nw + (w0 + jw);
+// entry "sta": weight-free, accepted only on its tuned grids; tile and window
+// sizes are not given there).  Tiles are 6x8x8 tokens, which both accepted
+// grids divide exactly; a query tile attends to the tiles of a (wt, wh, ww)
+// window that starts on each axis at clamp(c - (w-1)/2, 0, n - w) -- centred
+// where it fits, pushed inward at the edges.  The fine stage works on 1x8x8
+// slabs (64 tokens), six to a tile along t, so slab (st, sh, sw) of tile
+// (st/6, sh, sw) takes the 6*wt*wh*ww slabs of that tile's window, listed in
+// ascending order.  Threads [0, C*ks) write that slab plan (C slabs, ks
+// entries each); with tile_plan, threads past it write the tile-level plan
+// [tiles][wt*wh*ww] (tile id (tt*nh + th)*nw + tw) for the caller.
+__global__ void __launch_bounds__(256) wf_sta_plan(int* __restrict__ slab_plan, int* __restrict__ tile_plan,
+                                                   Grid3 g, int wt, int wh, int ww) {
+  constexpr int TT = 6;  // slabs per tile along t
+  const int kt = wt * wh * ww, ks = TT * kt, ntt = g.nt / TT;
+  const long id = (long)blockIdx.x * 256 + threadIdx.x, nslab = (long)g.C * ks;
+  if (id < nslab) {
+    const int c = (int)(id / ks), e = (int)(id % ks);
+    int st, sh, sw;
+    cube_coords(g, c, st, sh, sw);
+    const int t0 = min(max(st / TT - (wt - 1) / 2, 0), ntt - wt);
+    const int h0 = min(max(sh - (wh - 1) / 2, 0), g.nh - wh);
+    const int w0 = min(max(sw - (ww - 1) / 2, 0), g.nw - ww);
+    const int iw = e % ww, ih = (e / ww) % wh, js = e / (ww * wh);  // js = it * TT + slab within the tile
+    slab_plan[id] = ((t0 * TT + js) * g.nh + (h0 + ih)) * g.nw + (w0 + iw);
+  } else if (tile_plan && id < nslab + (long)ntt * g.nh * g.nw * kt) {
+    const long r = id - nslab;
+    const int c = (int)(r / kt), j = (int)(r % kt);
+    const int tw = c % g.nw, th = (c / g.nw) % g.nh, tt = c / (g.nw * g.nh);
+    const int t0 = min(max(tt - (wt - 1) / 2, 0), ntt - wt);
+    const int h0 = min(max(th - (wh - 1) / 2, 0), g.nh - wh);
+    const int w0 = min(max(tw - (ww - 1) / 2, 0), g.nw - ww);
+    const int jt = j / (wh * ww), jh = (j / ww) % wh, jw = j % ww;
+    tile_plan[r] = ((t0 + jt) * g.nh + (h0 + jh)) * g.nw + (w0 + jw);
+  }
 }
 
 // ---------------------------------------------------------------- plan check
@@ -577,7 +621,7 @@ __global__ void __launch_bounds__(256) wf_vsa_check_plan(const int* __restrict__
 
 // ---------------------------------------------------------------- host side
 VsaLayout vsa_layout(int BH, int T, int H, int W, int D) {
-  const Grid3 g = make_grid(T, H, W);
+  const Grid3 g = make_grid<Cube>(T, H, W);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   VsaLayout L{};
   L.C = g.C;
@@ -599,7 +643,7 @@ VsaLayout vsa_layout(int BH, int T, int H, int W, int D) {
 hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH, int T, int H,
                              int W, int D, float scale, int topk, double rope_theta,
                              int rope_precision, int* idx, float* scores_out, void* ws, hipStream_t s) {
-  const Grid3 g = make_grid(T, H, W);
+  const Grid3 g = make_grid<Cube>(T, H, W);
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   char* w = static_cast<char*>(ws);
   auto qc = reinterpret_cast<uint16_t*>(w + L.qc), kc = reinterpret_cast<uint16_t*>(w + L.kc),
@@ -669,7 +713,7 @@ hipError_t launch_vsa_check(const int* idx, int BH, int C, int topk, void* ws, s
 
 hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H, int W, int D,
                            float scale, int topk, int softmax_mode, float* o, float* lse, hipStream_t s) {
-  const Grid3 g = make_grid(T, H, W);
+  const Grid3 g = make_grid<Cube>(T, H, W);
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   const char* w = static_cast<const char*>(ws);
   auto go = [&](auto kernel) {
@@ -685,55 +729,55 @@ hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H,
   return wf_launch("wf_vsa_fine", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded>); });
 }
 
-// Sliding-tile attention workspace: the gather's regions, then the shared plan.
+// Sliding-tile attention workspace: the slab-ordered Q, K and V^T, then the slab plan shared by
+// all heads.  k is the window's tile count wt*wh*ww.
 StaLayout sta_layout(int BH, int T, int H, int W, int D, int k) {
-  const Grid3 g = make_grid(T, H, W);
+  const Grid3 g = make_grid<Slab>(T, H, W);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   StaLayout L{};
   const size_t tok = (size_t)BH * g.C * 64 * D * 2;
   L.qc = 0;
   L.kc = L.qc + up(tok);
   L.vct = L.kc + up(tok);
-  L.qbar = L.vct + up(tok);
-  L.kbar = L.qbar + up((size_t)BH * g.C * D * 4);
-  L.vbt = L.kbar + up((size_t)BH * g.C * D * 4);
-  L.plan = L.vbt + up((size_t)2 * BH * D * g.Cs * 2);
-  L.total = L.plan + up((size_t)g.C * k * 4);
+  L.plan = L.vct + up(tok);
+  L.total = L.plan + up((size_t)g.C * 6 * k * 4);
   return L;
 }
+
+int sta_slabs(int T, int H, int W) { return make_grid<Slab>(T, H, W).C; }
 
 hipError_t launch_sta(const void* q, const void* k, const void* v, int BH, int T, int H, int W, int D,
                       float scale, int wt, int wh, int ww, float* o, float* lse, int* plan_out, void* ws,
                       hipStream_t s) {
-  const Grid3 g = make_grid(T, H, W);
-  const int kk = wt * wh * ww;
-  const StaLayout L = sta_layout(BH, T, H, W, D, kk);
+  const Grid3 g = make_grid<Slab>(T, H, W);
+  const int kt = wt * wh * ww, ks = 6 * kt;
+  const StaLayout L = sta_layout(BH, T, H, W, D, kt);
   char* w = static_cast<char*>(ws);
   auto qc = reinterpret_cast<uint16_t*>(w + L.qc), kc = reinterpret_cast<uint16_t*>(w + L.kc),
        vct = reinterpret_cast<uint16_t*>(w + L.vct);
-  int* plan = plan_out ? plan_out : reinterpret_cast<int*>(w + L.plan);
-  hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
-    hipLaunchKernelGGL((wf_vsa_gather<128, 0>), dim3((unsigned)(BH * g.C)), dim3(256), 0, s,
+  int* plan = reinterpret_cast<int*>(w + L.plan);
+  hipError_t e = wf_launch("wf_sta_gather", s, [&] {
+    hipLaunchKernelGGL((wf_vsa_gather<128, 0, Slab, false>), dim3((unsigned)(BH * g.C)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), qc, kc, vct, reinterpret_cast<float*>(w + L.qbar),
-                       reinterpret_cast<float*>(w + L.kbar), reinterpret_cast<uint16_t*>(w + L.vbt), g, 0.0);
+                       static_cast<const uint16_t*>(v), qc, kc, vct, nullptr, nullptr, nullptr, g, 0.0);
   });
   if (e != hipSuccess) return e;
+  const long threads = (long)g.C * ks + (plan_out ? (long)(g.C / 6) * kt : 0);
   e = wf_launch("wf_sta_plan", s, [&] {
-    hipLaunchKernelGGL(wf_sta_plan, dim3((unsigned)(((long)g.C * kk + 255) / 256)), dim3(256), 0, s, plan, g,
+    hipLaunchKernelGGL(wf_sta_plan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, plan, plan_out, g,
                        wt, wh, ww);
   });
   if (e != hipSuccess) return e;
   return wf_launch("wf_sta_fine", s, [&] {
-    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, false, kSoftmaxGuarded>), dim3((unsigned)(BH * g.C)), dim3(128), 0, s,
-                       qc, kc, vct, plan, o, lse, nullptr, nullptr, g, kk, 0L, scale * kLog2e);
+    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Slab>), dim3((unsigned)(BH * g.C)), dim3(128),
+                       0, s, qc, kc, vct, plan, o, lse, nullptr, nullptr, g, ks, 0L, scale * kLog2e);
   });
 }
 
 hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int BH, int T, int H,
                                  int W, int D, float scale, int topk, float* o, float* lse,
                                  float* o_coarse, hipStream_t s) {
-  const Grid3 g = make_grid(T, H, W);
+  const Grid3 g = make_grid<Cube>(T, H, W);
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   char* w = static_cast<char*>(ws);
   float* oc = o_coarse ? o_coarse : reinterpret_cast<float*>(w + L.ocoarse);

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wf_tiles.hpp"
+
 namespace wf {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -36,14 +38,6 @@ __device__ __forceinline__ int xcd_remap(int wg, int G) {
   const int q = G / kNumXcd, r = G % kNumXcd;
   const int x = wg % kNumXcd, i = wg / kNumXcd;
   return x * q + min(x, r) + i;
-}
-
-// Key order used for V^T tiles inside every group of 16 keys: keys 4..7 and
-// 8..11 trade places (bits 2 and 3 of the index swap; an involution).  It is
-// the order in which a 32x32 MFMA result holds its rows in one lane pair, so
-// the probabilities feed the PV product straight from the score registers.
-__host__ __device__ constexpr int perm16(int n) {
-  return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -90,20 +84,7 @@ struct P4 {
 };
 
 // ------------------------------------------------------------------ LDS tiles
-// A K tile is [64 keys][D] bf16 and a V^T tile [D][64 keys] bf16, both
-// unpadded.  Each 16-byte chunk is XOR-swizzled within its row so that the 16
-// lanes of one ds_read_b128 quarter-wave (one chunk of 16 consecutive rows)
-// hit 16 distinct 16-byte bank groups of gfx950's 64-bank LDS.
-template <int D>
-struct Swz {
-  static constexpr int KB = 64 * D * 2;  // K tile bytes
-  static constexpr int VB = D * 64 * 2;  // V^T tile bytes
-  static constexpr int KCPR = D / 8;     // 16-byte chunks per K row
-  __host__ __device__ static constexpr int kslot(int r, int c) {
-    return KCPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
-  }
-  __host__ __device__ static constexpr int vslot(int d, int c) { return c ^ ((d >> 1) & 7); }
-};
+// (tile layout and copy offsets: wf_tiles.hpp)
 
 // Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes
 // return zero instead of touching memory (gfx9 range check on the VGPR offset).
@@ -111,29 +92,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Global->LDS tile copies.  Wavefront w of NWC copies K pieces g = i * NWC + w
-// (i < KPW), each 1 KiB of the K tile's LDS image: lane L fetches the 16-byte
-// chunk that belongs at LDS byte g * 1024 + 16 L under the K swizzle.  The
-// swizzle depends on the row only through r & 15, so the lane's global offset
-// repeats with period KPER pieces up to a uniform step of KPER * NWC KiB; V^T
-// pieces likewise repeat every piece up to a uniform step of NWC * 8 rows.
-// Only KPER + 1 per-lane offsets are kept in registers.
+// Per-lane offsets of the global->LDS tile copies (CopyGeom): only KPER + 1
+// per-lane offsets are kept in registers.
 template <int D, int NWC>
 struct CopyOffsets {
-  static constexpr int CPR = Swz<D>::KCPR, RPP = 64 / CPR;  // 16-byte chunks per K row, K rows per piece
-  static constexpr int KPW = Swz<D>::KB / 1024 / NWC, VPW = Swz<D>::VB / 1024 / NWC;
-  static constexpr int KPER = (NWC * RPP) % 16 == 0 ? 1 : (2 * NWC * RPP) % 16 == 0 ? 2 : 4;
-  static_assert(KPW % KPER == 0, "pieces per wavefront");
-  static_assert((NWC * 8) % 16 == 0, "V^T swizzle must repeat every piece");
+  using G = CopyGeom<D, NWC>;
+  static constexpr int KPW = G::KPW, VPW = G::VPW, KPER = G::KPER;
   uint32_t k[KPER], v;
   __device__ __forceinline__ CopyOffsets(int w, int lane, int vld) {
 #pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int P = (i * NWC + w) * 64 + lane, r = P / CPR, c = Swz<D>::kslot(r, P % CPR);
-      k[i] = (uint32_t)(r * D * 2 + c * 16);
-    }
-    const int d = w * 8 + lane / 8, c = Swz<D>::vslot(d, lane % 8);
-    v = (uint32_t)(d * vld * 2 + c * 16);
+    for (int i = 0; i < KPER; ++i) k[i] = G::k_lane(i, w, lane);
+    v = G::v_lane(w, lane, vld);
   }
 };
 
@@ -149,7 +118,7 @@ __device__ __forceinline__ void tile_copy(const CopyOffsets<D, NWC>& off, const 
                                           int w) {
   using CO = CopyOffsets<D, NWC>;
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  constexpr int KSTEP = CO::KPER * NWC * 1024;  // global bytes between pieces i and i + KPER
+  constexpr int KSTEP = CO::G::KSTEP;  // global bytes between pieces i and i + KPER
   if (kg) {  // one descriptor per KPER-piece step, bounded at row krows (scalar work only)
 #pragma unroll
     for (int i = 0; i < CO::KPW; ++i) {
@@ -165,7 +134,36 @@ __device__ __forceinline__ void tile_copy(const CopyOffsets<D, NWC>& off, const 
 #pragma unroll
     for (int i = 0; i < CO::VPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vdst + (i * NWC + w) * 1024), 16, (int)off.v,
-                                               i * NWC * 8 * vld * 2, 0, 0);
+                                               (int)CO::G::v_step(i, vld), 0, 0);
+  }
+}
+
+// Copy the K tile and/or the V^T tile of key cube `cube` (K [C][64][D], V^T
+// [C][D][64], one head's cube-ordered regions) into LDS.  The descriptors
+// cover the head's whole region (C cubes) and the cube's byte offset goes into
+// the per-lane offset, which the hardware range-checks: cube_offset maps an
+// index outside [0, C) to the region's end, so a bad plan entry reads zeros
+// and never touches memory outside the region.
+template <int D, int NWC>
+__device__ __forceinline__ void cube_copy(const CopyOffsets<D, NWC>& off, const uint16_t* khead, char* kdst,
+                                          const uint16_t* vhead, char* vdst, int cube, int C, int w) {
+  using CO = CopyOffsets<D, NWC>;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  constexpr uint32_t CB = 64u * D * 2;  // bytes of one cube of K (or V^T)
+  const uint32_t region = (uint32_t)C * CB, at = cube_offset(cube, C, CB);
+  if (khead) {
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(khead, region);
+#pragma unroll
+    for (int i = 0; i < CO::KPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kdst + (i * NWC + w) * 1024), 16,
+                                               (int)(off.k[i % CO::KPER] + at), (int)CO::G::k_step(i), 0, 0);
+  }
+  if (vhead) {
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vhead, region);
+#pragma unroll
+    for (int i = 0; i < CO::VPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vdst + (i * NWC + w) * 1024), 16, (int)(off.v + at),
+                                               (int)CO::G::v_step(i, 64), 0, 0);
   }
 }
 

@@ -49,12 +49,14 @@ hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int
                                  int W, int D, float scale, int topk, float* o, float* lse,
                                  float* o_coarse, hipStream_t s);
 
-// Sliding-tile attention over the cube layout: gather, the (wt, wh, ww)-window plan
-// (plan_out, int32 [C][wt*wh*ww], or the workspace when null), fine stage.
+// Sliding-tile attention: 6x8x8-token tiles, a (wt, wh, ww)-tile window per query tile; the
+// gather into 1x8x8 slabs, the slab plan (and the tile plan into plan_out, int32
+// [tiles][wt*wh*ww], when not null), the fine stage.  Grids must be whole tiles.
 struct StaLayout {
-  size_t qc, kc, vct, qbar, kbar, vbt, plan, total;
+  size_t qc, kc, vct, plan, total;
 };
 StaLayout sta_layout(int BH, int T, int H, int W, int D, int k);
+int sta_slabs(int T, int H, int W);
 hipError_t launch_sta(const void* q, const void* k, const void* v, int BH, int T, int H, int W, int D,
                       float scale, int wt, int wh, int ww, float* o, float* lse, int* plan_out, void* ws,
                       hipStream_t s);
