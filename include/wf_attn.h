@@ -98,6 +98,26 @@ int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, flo
                       int32_t B, int32_t Hh, int32_t N, int32_t D, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Dense attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and result bits as wf_attn_dense, with the transposed
+ * V kept in the library's own static scratch instead of a caller workspace.
+ * The scratch is one file-scope device array of WF_DENSE_NOALLOC_SCRATCH_BYTES
+ * per GPU, taken on that GPU's first call and held until the process ends; the
+ * call allocates and frees nothing.  Every call on a GPU uses the same array,
+ * so calls that overlap on one GPU (another stream, another thread) race and
+ * must be serialised by the caller; calls in one stream are ordered as usual.
+ *
+ *   Arguments as wf_attn_dense, without the workspace.  Sizes whose
+ *   wf_attn_dense_workspace_bytes() exceeds WF_DENSE_NOALLOC_SCRATCH_BYTES
+ *   (128 MiB: e.g. up to 16 heads of 32,760 tokens at D = 128) return
+ *   WF_ERR_WORKSPACE with nothing enqueued.
+ */
+#define WF_DENSE_NOALLOC_SCRATCH_BYTES (128u << 20)
+int32_t wf_attn_dense_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                              int32_t B, int32_t Hh, int32_t N, int32_t D, float scale, void* stream);
+
 /* -------------------------------------------------------------------- VSA */
 
 /* Number of 4x4x4 cubes of a T x H x W grid after padding each side up to a

@@ -25,7 +25,7 @@ def wf():
 def test_every_declared_symbol_is_exported(wf):
     names = declared_functions()
     assert "wf_attn_dense" in names and "wf_vsa_coarse_topk" in names and "wf_vsa_fine" in names
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(wf.lib, n), f"{n} declared in wf_attn.h but not exported"
 

@@ -29,6 +29,7 @@ _SIGS = {
     "wf_attn_dense_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "wf_attn_dense": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
     "wf_attn_dense_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "wf_attn_dense_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp]),
     "wf_vsa_fine_ex": (_i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp]),
     "wf_vsa_num_cubes": (_i32, [_i32, _i32, _i32]),
     "wf_vsa_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -159,6 +160,20 @@ def wf_attn_dense(q, k, v, scale: Optional[float] = None, with_lse: bool = False
         _check(lib.wf_attn_dense_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
                                     B, Hh, N, D, scale, int(softmax_mode), ws.data_ptr(),
                                     ws.numel() * ws.element_size(), _stream_handle(q.device)), "wf_attn_dense_ex")
+    return out, lse
+
+
+def wf_attn_dense_noalloc(q, k, v, out, lse=None, scale: Optional[float] = None):
+    """Dense attention through wf_attn_dense_noalloc: the library's static per-GPU scratch holds the
+    transposed V, so the call allocates nothing.  out (and lse) must be given."""
+    torch = _torch()
+    _qkv_check(q, k, v)
+    B, Hh, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _expect(out, "out", (B, Hh, N, D), torch.float32, q.device)
+    _expect(lse, "lse", (B, Hh, N), torch.float32, q.device)
+    _check(lib.wf_attn_dense_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
+                                     B, Hh, N, D, scale, _stream_handle(q.device)), "wf_attn_dense_noalloc")
     return out, lse
 
 

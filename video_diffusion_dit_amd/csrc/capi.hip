@@ -131,9 +131,9 @@ size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D
   return wf::dense_workspace_bytes(B * Hh, N, D);
 }
 
-static int32_t dense(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
-                     int32_t Hh, int32_t N, int32_t D, float scale, int32_t softmax_mode,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks shared by the dense entry points (everything but the workspace).
+static int32_t dense_checks(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
+                            int32_t Hh, int32_t N, int32_t D, float scale) {
   WF_CHECK_PTR(q);
   WF_CHECK_PTR(k);
   WF_CHECK_PTR(v);
@@ -149,6 +149,13 @@ static int32_t dense(const void* q, const void* k, const void* v, float* o, floa
     return fail(WF_ERR_UNSUPPORTED, "N=%d D=%d: one head's K and V^T must stay below 2 GiB", N, D);
   if (!isfinite(scale) || !(scale > 0.f))
     return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
+  return WF_OK;
+}
+
+static int32_t dense(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
+                     int32_t Hh, int32_t N, int32_t D, float scale, int32_t softmax_mode,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (int32_t st = dense_checks(q, k, v, o, lse, B, Hh, N, D, scale)) return st;
   const size_t need = wf::dense_workspace_bytes(B * Hh, N, D);
   if (!workspace || workspace_bytes < need)
     return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
@@ -165,6 +172,18 @@ int32_t wf_attn_dense(const void* q, const void* k, const void* v, float* o, flo
                       size_t workspace_bytes, void* stream) {
   return dense(q, k, v, o, lse, B, Hh, N, D, scale, WF_SOFTMAX_GUARDED, workspace, workspace_bytes,
                stream);
+}
+
+int32_t wf_attn_dense_noalloc(const void* q, const void* k, const void* v, float* o, float* lse, int32_t B,
+                              int32_t Hh, int32_t N, int32_t D, float scale, void* stream) {
+  if (int32_t st = dense_checks(q, k, v, o, lse, B, Hh, N, D, scale)) return st;
+  const size_t need = wf::dense_workspace_bytes(B * Hh, N, D);
+  if (need > (size_t)WF_DENSE_NOALLOC_SCRATCH_BYTES)
+    return fail(WF_ERR_WORKSPACE, "B=%d Hh=%d N=%d D=%d needs %zu bytes of scratch; the static scratch holds %zu",
+                B, Hh, N, D, need, (size_t)WF_DENSE_NOALLOC_SCRATCH_BYTES);
+  hipError_t e = wf::launch_dense_noalloc(q, k, v, o, lse, B * Hh, N, D, scale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dense (static scratch) launch");
+  return ok();
 }
 
 static bool softmax_mode_ok(int32_t mode) {

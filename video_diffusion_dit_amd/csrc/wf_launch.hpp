@@ -29,6 +29,10 @@ size_t dense_workspace_bytes(int BH, int N, int D);
 // softmax_mode: 0 guarded integer reference, 1 running max, 2 fixed first-tile reference.
 hipError_t launch_dense(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
                         int N, int D, float scale, int softmax_mode, void* ws, hipStream_t s);
+// The same with the library's static per-GPU scratch (noalloc.hip) as the workspace; the caller
+// has checked dense_workspace_bytes() against its size.
+hipError_t launch_dense_noalloc(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
+                                int N, int D, float scale, hipStream_t s);
 
 // VSA workspace layout (byte offsets, each 256-byte aligned).
 struct VsaLayout {
