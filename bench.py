@@ -76,6 +76,9 @@ def parse():
                    help="skip timing the CPU oracle (used for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="also time the oracle per measured configuration (whole calls where they take "
+                        "seconds to a minute, one head scaled otherwise) and add the record 'cpu_oracle_calls'")
     p.add_argument("--traffic-json", metavar="ROCPROF_DIR", default=None,
                    help="write the dense kernel's calibrated traffic, clock and MFMA busy fraction from a "
                         "rocprofv3 run directory to profiles/ and exit (no GPU)")
@@ -91,10 +94,20 @@ def parse():
 
 
 def git_rev() -> str:
+    """The source revision: git's, or (where the tree travels without .git) the one the build
+    step recorded next to the library it built."""
     try:
-        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
-                              text=True, timeout=10).stdout.strip() or "unknown"
+        rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                             text=True, timeout=10).stdout.strip()
+        if rev:
+            return rev
     except Exception:
+        pass
+    try:
+        with open(os.path.join(ROOT, "video_diffusion_dit_amd", "build_info.json")) as f:
+            info = json.load(f)
+        return info.get("git", "unknown") + ("+dirty" if info.get("dirty") else "") + " (recorded at build)"
+    except (OSError, ValueError):
         return "unknown"
 
 
@@ -106,6 +119,15 @@ def vsa_flops(wl, C) -> dict:
     fine = 4.0 * wl.B * wl.Hh * wl.N * 64 * wl.topk * wl.D        # padded queries excluded
     coarse = 2.0 * wl.B * wl.Hh * C * C * wl.D
     return dict(fine=fine, coarse=coarse, total=fine + coarse)
+
+
+IDEAL_CONVENTION = ("dense FLOPs / VSA FLOPs at the same shape, real tokens: 4 N^2 D / (4 N (64 k) D + "
+                    "2 C^2 D) per head (gather, top-k and padding excluded)")
+
+
+def ideal_speedup(wl, C) -> float:
+    """The dense call's FLOPs over the VSA call's (fine on real queries + coarse scores), per head."""
+    return dense_flops(wl) / vsa_flops(wl, C)["total"]
 
 
 def vsa_bytes(wl, C) -> dict:
@@ -122,6 +144,18 @@ def vsa_bytes(wl, C) -> dict:
     return dict(gather=gather, scores=scores, topk=topk, coarse_out=coarse_out, merge=merge)
 
 
+def blas_info() -> dict:
+    """The BLAS numpy's matrix products run on, and its thread count."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"library": f"{i.get('internal_api')} {i.get('version')}", "threads": int(i.get("num_threads", 1))}
+    except Exception:
+        pass
+    return {"library": "unknown", "threads": os.cpu_count() or 1}
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The fp64 oracle on a bounded sample of the step's workload, about `seconds` of CPU.
 
@@ -129,14 +163,9 @@ def cpu_baseline(seconds: float) -> dict:
     (pool, scores, top-k, fine) of the VSA workload; the rate is the step's FLOPs over
     the step's time extrapolated from the per-head times, the same convention as
     `value`."""
-    import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        threads = os.cpu_count() or 1
+    blas = blas_info()
     wd, wv = synth.WORKLOADS[DENSE], synth.WORKLOADS[VSA]
 
     def heads_within(wl, budget, run, least=1):
@@ -159,12 +188,61 @@ def cpu_baseline(seconds: float) -> dict:
     C = int(oracle.geometry(wv.T, wv.H, wv.W)["C"])
     step_flops = dense_flops(wd) + vsa_flops(wv, C)["total"]
     step_s = td / nd * wd.B * wd.Hh + tv / nv * wv.B * wv.Hh
-    return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle: dense attention of {nd} whole head(s) ({wd.N} x {wd.N} x d{wd.D}) "
-                      f"of the {DENSE} workload in {td:.1f} s, and the whole VSA pass of {nv} head(s) of the "
-                      f"{VSA} workload (top-{wv.topk} of {C} cubes) in {tv:.1f} s; one step extrapolated: "
-                      f"{step_s:.0f} s",
-            "host_cpus": os.cpu_count()}
+    return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": blas["threads"], "kind": "oracle",
+            "sample": f"fp64 numpy oracle ({blas['library']}, {blas['threads']} threads): dense attention of "
+                      f"{nd} whole head(s) ({wd.N} x {wd.N} x d{wd.D}) of the {DENSE} workload in {td:.1f} s, and "
+                      f"the whole VSA pass of {nv} head(s) of the {VSA} workload (top-{wv.topk} of {C} cubes) in "
+                      f"{tv:.1f} s; one step extrapolated: {step_s:.0f} s",
+            "blas": blas["library"], "host_cpus": os.cpu_count()}
+
+
+def cpu_oracle_calls() -> dict:
+    """The fp64 oracle per measured configuration: whole calls of the 512-token, 12-head 480p
+    and VSA 480p workloads, and one (batch, head) of the CFG-pair and 720p workloads scaled by
+    their head counts (labelled extrapolated).  Minutes of CPU; run on request (--cpu-full)."""
+    import oracle
+    import synth
+    blas = blas_info()
+    out = {"blas": blas["library"], "threads": blas["threads"], "host_cpus": os.cpu_count(), "configs": {}}
+
+    def slices(wl, heads):
+        phi = synth.field_for(wl)
+        for b, h in heads:
+            yield tuple(synth.bits_to_f64(synth.make_slice(wl, t, b, h, phi)) for t in ("q", "k", "v"))
+
+    def dense_call(name, heads):
+        wl = synth.WORKLOADS[name]
+        dt = 0.0
+        for q, k, v in slices(wl, heads):
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, wl.scale)
+            dt += time.perf_counter() - t0
+        return wl, dt
+
+    def vsa_call(name, heads):
+        wl = synth.WORKLOADS[name]
+        dt = 0.0
+        for q, k, v in slices(wl, heads):
+            t0 = time.perf_counter()
+            oracle.vsa(q, k, v, wl.T, wl.H, wl.W, wl.topk, wl.scale)
+            dt += time.perf_counter() - t0
+        return wl, dt
+
+    for name, kind, whole in (("dense_512_iid", "dense", True), ("dense_480p_12h", "dense", True),
+                              ("dense_480p_cfg", "dense", False), ("vsa_480p", "vsa", True),
+                              ("dense_720p_cfg", "dense", False), ("vsa_720p", "vsa", False)):
+        wl = synth.WORKLOADS[name]
+        heads = [(b, h) for b in range(wl.B) for h in range(wl.Hh)] if whole else [(0, 0)]
+        wl, dt = (dense_call if kind == "dense" else vsa_call)(name, heads)
+        C = int(oracle.geometry(wl.T, wl.H, wl.W)["C"])
+        flops = dense_flops(wl) if kind == "dense" else vsa_flops(wl, C)["total"]
+        call_s = dt if whole else dt * wl.B * wl.Hh
+        print(f"cpu oracle {name}: {call_s:.1f} s per call ({'whole call' if whole else 'extrapolated from one head'})",
+              file=sys.stderr, flush=True)
+        out["configs"][name] = {"seconds_per_call": call_s, "measured": "whole call" if whole else
+                                f"one (b, h) of {wl.B * wl.Hh}, scaled (extrapolated)",
+                                "tflops": flops / call_s / 1e12}
+    return out
 
 
 def _short(name: str) -> str:
@@ -503,7 +581,7 @@ def main():
                 "dense_frac_bf16_peak": dense_flops(wd7) / (k7ms["wf_dense_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                 "vsa_ms_per_call": v7ms,
                 "vsa_fine_tflops": f7["fine"] / (k7ms["wf_vsa_fine"] * 1e-3) / 1e12,
-                "dense_equivalent_speedup": d7 / v7ms, "ideal_speedup": C7 / wv7.topk,
+                "dense_equivalent_speedup": d7 / v7ms, "ideal_speedup": ideal_speedup(wv7, C7),
                 "kernel_ms": k7ms}
         del q7, k7, v7, o7, wsd7, wsv7, idx7
 
@@ -611,7 +689,8 @@ def main():
             "scores_gbs": by_v["scores"] / (kern["wf_vsa_scores"] * 1e-3) / 1e9,
             "dense_equivalent_speedup": ms_dense_same / ms_vsa,
             "dense_equivalent_tflops": fl_d * wv.B / wd.B / (ms_vsa * 1e-3) / 1e12,
-            "ideal_speedup": C / wv.topk,
+            "ideal_speedup": ideal_speedup(wv, C),
+            "ideal_speedup_convention": IDEAL_CONVENTION,
         },
         "vsa_gated": None if gated_ms is None else {
             "topk": wv.topk,
@@ -632,6 +711,7 @@ def main():
             "kernel_ms": k78_ms,
             "fine_tflops_page_convention": 4.0 * wv.N * 64 * k78 * wv.D * wv.Hh / (k78_ms["wf_vsa_fine"] * 1e-3) / 1e12,
             "dense_equivalent_speedup": ms_dense_same / sum(k78_ms.values()),
+            "ideal_speedup": ideal_speedup(synth.WORKLOADS["vsa_480p_k78"], C),
         },
         "per_gpu_share": share,
         "context": {"pages_dense_ms_b200": 17.0,
@@ -643,6 +723,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if args.cpu_full:
+        out["cpu_oracle_calls"] = cpu_oracle_calls()
     print(json.dumps(out), flush=True)
 
 

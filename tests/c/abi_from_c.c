@@ -19,7 +19,7 @@ static int failures = 0;
 int main(void) {
   char buf[64];
   void* const fake = (void*)(size_t)0x10000; /* aligned, never dereferenced */
-  EXPECT(wf_abi_version() == 2);
+  EXPECT(wf_abi_version() == 3);
   EXPECT(strcmp(wf_status_string(WF_OK), "WF_OK") == 0);
   EXPECT(strcmp(wf_status_string(WF_ERR_WORKSPACE), "WF_ERR_WORKSPACE") == 0);
   EXPECT(wf_vsa_num_cubes(21, 30, 52) == 624);

@@ -34,7 +34,7 @@ def test_status_strings(wf):
     assert wf.lib.wf_status_string(0) == b"WF_OK"
     assert wf.lib.wf_status_string(4) == b"WF_ERR_BAD_INDEX"
     assert wf.lib.wf_status_string(99) == b"WF_UNKNOWN_STATUS"
-    assert wf.lib.wf_abi_version() == 2
+    assert wf.lib.wf_abi_version() == 3
 
 
 def test_geometry_queries(wf):

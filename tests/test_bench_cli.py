@@ -88,3 +88,16 @@ def test_reported_vsa_flops_follow_the_page_convention():
     # the step's own top-32 figure scales with k
     wl32 = synth.WORKLOADS["vsa_480p"]
     assert bench.vsa_flops(wl32, golden["cubes"])["fine"] * 78 == fl["fine"] * 32
+
+
+def test_ideal_speedup_is_the_flop_ratio():
+    """Dense FLOPs over VSA FLOPs (fine on real queries + coarse scores) at the same shape."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    w480, w720 = synth.WORKLOADS["vsa_480p"], synth.WORKLOADS["vsa_720p"]
+    assert abs(bench.ideal_speedup(w480, 624) - 32760 / (64 * 32 + 624 ** 2 / (2 * 32760))) < 1e-9
+    assert 15.9 < bench.ideal_speedup(w480, 624) < 16.0
+    assert 18.3 < bench.ideal_speedup(w720, 1440) < 18.5
+    info = bench.blas_info()
+    assert info["threads"] >= 1 and isinstance(info["library"], str)

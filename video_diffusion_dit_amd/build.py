@@ -39,6 +39,27 @@ def _compile(src: str, extra: list) -> str:
     return obj
 
 
+def _record_revision() -> None:
+    """Write the source revision next to the library, for runs on copies of the tree that carry
+    no .git (the benchmark reports it)."""
+    import json
+    info = {"git": "unknown", "dirty": False}
+    try:
+        rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                             text=True, timeout=10)
+        if rev.returncode == 0 and rev.stdout.strip():
+            info["git"] = rev.stdout.strip()
+            st = subprocess.run(["git", "status", "--porcelain", "--untracked-files=no", "--",
+                                 os.path.relpath(CSRC, ROOT), os.path.relpath(INCLUDE, ROOT)],
+                                cwd=ROOT, capture_output=True, text=True, timeout=10)
+            info["dirty"] = bool(st.stdout.strip())
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(PKG, "build_info.json"), "w") as f:
+        json.dump(info, f)
+        f.write("\n")
+
+
 def build(extra: list | None = None) -> str:
     """Compile every source and link the shared library; returns its path."""
     extra = list(extra or [])
@@ -51,6 +72,7 @@ def build(extra: list | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    _record_revision()
     return LIB
 
 

@@ -124,7 +124,7 @@ const char* wf_status_string(int32_t status) {
 
 const char* wf_last_error_detail(void) { return g_detail.c_str(); }
 
-int32_t wf_abi_version(void) { return 2; }
+int32_t wf_abi_version(void) { return 3; }
 
 size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D) {
   if (!sizes_ok(B, Hh, N, D)) return 0;
