@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwfattn.so")
+# WF_LIB_PATH selects another build of the same library (the host-sanitizer build the CPU tests
+# make); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("WF_LIB_PATH") or os.path.join(_HERE, "libwfattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m video_diffusion_dit_amd.build` "
