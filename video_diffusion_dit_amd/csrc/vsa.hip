@@ -7,6 +7,8 @@
 // top-k key cubes of every query cube, then run token-level attention of each
 // query cube over those cubes only.  Section "Roofline analysis set the 3.35
 // ms target" counts one output tile per (query cube, head).
+#include <type_traits>
+
 #include "wf_attn.h"
 #include "wf_device.hpp"
 #include "wf_launch.hpp"
@@ -422,19 +424,42 @@ __global__ void __launch_bounds__(256) wf_vsa_coarse_out(const float* __restrict
   }
 }
 
+// Gate rows and the query cube's coarse output for the gated merge, loaded
+// into registers ahead of the epilogue (lane L takes 4 head dims, chunk L % 32,
+// of rows 2i + L/32 of its wavefront's 32 query slots).  Padded slots load
+// the cube's first row instead (read, never used), so every lane issues the
+// same loads.
+struct GatePre {
+  uint2 g[16];
+  float4 c4;
+};
+
+template <int D, class BLK>
+__device__ __forceinline__ void gate_prefetch(GatePre& gp, const Grid3& g, int ct, int ch, int cw, int wave,
+                                              int lane, long head_row0, const uint16_t* __restrict__ gate,
+                                              const float* __restrict__ ocube) {
+  const int c = lane % 32;
+  const int tok0 = slot_token<BLK>(g, ct, ch, cw, 0);  // slot 0 is always a real token
+  gp.c4 = *reinterpret_cast<const float4*>(ocube + c * 4);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tok = slot_token<BLK>(g, ct, ch, cw, wave * 32 + 2 * i + lane / 32);
+    gp.g[i] = *reinterpret_cast<const uint2*>(gate + (head_row0 + (tok >= 0 ? tok : tok0)) * D + c * 4);
+  }
+}
+
 // Fine-stage epilogue: the normalised output rows of a wavefront go through
 // its own LDS slot (32 rows x D fp32 = 16 KiB, the K or V slot, free once the
 // sweep is done), so that global stores cover two whole token rows per
 // instruction instead of 16 bytes of 32 different rows.  In LDS, row r's
 // 16-byte chunk c sits at chunk c ^ (r % 32), which keeps both the scattered
 // writes and the row reads free of bank conflicts.  With GATED the merge
-// O = O_fine + gate * Oc is applied on the way out, where the gate is read
-// row-contiguously as well.
+// O = O_fine + gate * Oc is applied on the way out, from the gate rows
+// prefetched into gp.
 template <int D, bool GATED, class BLK>
 __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* slot_lds, int j, int half,
                                               const Grid3& g, int ct, int ch, int cw, int wave, long head_row0,
-                                              float* __restrict__ out, const uint16_t* __restrict__ gate,
-                                              const float* __restrict__ ocube) {
+                                              float* __restrict__ out, const GatePre& gp) {
   constexpr int DB = D / 32, CH = D / 4;  // 16-byte chunks per row
   static_assert(CH == 32, "row swizzle assumes 32 chunks per row");
   float* lds = reinterpret_cast<float*>(slot_lds);
@@ -448,7 +473,7 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
     }
   asm volatile("" ::: "memory");  // this wavefront's LDS writes precede its reads (LDS keeps wave order)
   const int lane = half * 32 + j, c = lane % 32;
-#pragma unroll 4
+#pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = 2 * i + lane / 32;  // row inside this wavefront's 32
     const int tok = slot_token<BLK>(g, ct, ch, cw, wave * 32 + r);
@@ -456,12 +481,11 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
     if (tok >= 0) {
       const long row = head_row0 + tok;
       if constexpr (GATED) {
-        const float4 c4 = *reinterpret_cast<const float4*>(ocube + c * 4);
-        const uint2 g2 = *reinterpret_cast<const uint2*>(gate + row * D + c * 4);
-        v.x = __builtin_fmaf(__uint_as_float(g2.x << 16), c4.x, v.x);
-        v.y = __builtin_fmaf(__uint_as_float(g2.x & 0xFFFF0000u), c4.y, v.y);
-        v.z = __builtin_fmaf(__uint_as_float(g2.y << 16), c4.z, v.z);
-        v.w = __builtin_fmaf(__uint_as_float(g2.y & 0xFFFF0000u), c4.w, v.w);
+        const uint2 g2 = gp.g[i];
+        v.x = __builtin_fmaf(__uint_as_float(g2.x << 16), gp.c4.x, v.x);
+        v.y = __builtin_fmaf(__uint_as_float(g2.x & 0xFFFF0000u), gp.c4.y, v.y);
+        v.z = __builtin_fmaf(__uint_as_float(g2.y << 16), gp.c4.z, v.z);
+        v.w = __builtin_fmaf(__uint_as_float(g2.y & 0xFFFF0000u), gp.c4.w, v.w);
       }
       *reinterpret_cast<float4*>(out + row * D + c * 4) = v;
     }
@@ -524,12 +548,24 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, cur, g.C, wave);
   cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cur, g.C, wave);
   wait_tile_copies_keep<VP>();  // K(0) landed; V(0) may still fly
-  for (int t = 0; t < k; ++t) {
+  int ct, ch, cw;
+  cube_coords(g, c, ct, ch, cw);
+  const long head_row0 = (long)bh * g.T * g.H * g.W;
+  GatePre gp;
+  // One tile.  LAST (the gated kernel's final tile, peeled off the loop) issues no copies of a next
+  // cube; instead, once the scores are done and Q is no longer needed, it loads the gate rows and
+  // the coarse output for the epilogue, so their latency hides behind the softmax.
+  auto tile = [&](int t, auto last_c) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_c)::value;
     barrier_nofence();  // K(t) visible
     mfma_run<D, NPV, NPV + NQK>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
     barrier_nofence();                                                     // K slot free
     const int nxt = t + 1 < k ? plan[t + 1] : cur;  // past the end: a harmless copy of the last cube
-    cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, nxt, g.C, wave);
+    if constexpr (LAST) {
+      gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
+    } else {
+      cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, nxt, g.C, wave);
+    }
     int kt, kh, kw;
     cube_coords(g, cur, kt, kh, kw);
     const int lt = g.T - BLK::BT * kt, lh = g.H - BLK::BH * kh, lw = g.W - BLK::BW * kw;
@@ -543,22 +579,29 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
       }
     }
     softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, p2);
-    wait_tile_copies_keep<KP>();  // V(t) landed (it had the scores and the softmax to do so); K(t+1) may fly
+    if constexpr (LAST)
+      wait_tile_copies();          // V(t) landed, and the gate rows
+    else
+      wait_tile_copies_keep<KP>();  // V(t) landed (it had the scores and the softmax to do so); K(t+1) may fly
     barrier_nofence();            // V(t) visible
     mfma_run<D, 0, NPV>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // O += P V(t)
     barrier_nofence();                                             // V slot free
-    cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, nxt, g.C, wave);
-    wait_tile_copies_keep<VP>();  // K(t+1) landed; V(t+1) may fly
+    if constexpr (!LAST) {
+      cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, nxt, g.C, wave);
+      wait_tile_copies_keep<VP>();  // K(t+1) landed; V(t+1) may fly
+    }
     cur = nxt;
+  };
+  if constexpr (GATED) {
+    for (int t = 0; t < k - 1; ++t) tile(t, std::false_type());
+    tile(k - 1, std::true_type());
+  } else {
+    for (int t = 0; t < k; ++t) tile(t, std::false_type());
   }
   wait_tile_copies();  // this wavefront's copies (the last ones are redundant) have landed
   barrier_nofence();   // every wavefront is done with both slots
-  int ct, ch, cw;
-  cube_coords(g, c, ct, ch, cw);
-  const long head_row0 = (long)bh * g.T * g.H * g.W;
   const float lt = l + __shfl_xor(l, 32);
-  fine_epilogue<D, GATED, BLK>(oacc, 1.f / lt, wave == 0 ? ks : vs, j, half, g, ct, ch, cw, wave, head_row0, o,
-                               gate, GATED ? ocoarse + (cube_base + c) * D : nullptr);
+  fine_epilogue<D, GATED, BLK>(oacc, 1.f / lt, wave == 0 ? ks : vs, j, half, g, ct, ch, cw, wave, head_row0, o, gp);
   const int tok = slot_token<BLK>(g, ct, ch, cw, slot);
   if (lse && tok >= 0 && half == 0) lse[head_row0 + tok] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
 }
