@@ -39,7 +39,8 @@ VSA = "vsa_480p"
 # HBM traffic of the dense kernel, measured with rocprofv3 FETCH_SIZE / WRITE_SIZE; used only while
 # the kernel sources hash to the value recorded with the measurement
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_fwd_480p_cfg.json")
-DENSE_SOURCES = [os.path.join(ROOT, "video_diffusion_dit_amd", "csrc", f) for f in ("dense.hip", "wf_device.hpp")]
+DENSE_SOURCES = [os.path.join(ROOT, "video_diffusion_dit_amd", "csrc", f)
+                 for f in ("dense.hip", "wf_device.hpp", "wf_tiles.hpp")]
 
 
 def sources_sha256(paths) -> str:
