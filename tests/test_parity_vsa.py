@@ -203,6 +203,33 @@ def test_vsa_fine_caller_plan_and_validation(wf, monkeypatch):
     monkeypatch.delenv("WF_VALIDATE")
 
 
+@pytest.mark.parametrize("plan", [[6], [4], [2], [18], [6, 9], [0, 6], [6, 9, 10], [2, 9, 10], [18, 19, 21],
+                                  [0, 1, 6], [6, 7, 8], [17, 25, 26]])
+def test_vsa_fine_edge_cube_plans(wf, plan):
+    """The same caller plan for every query cube of a 9x10x11 grid (27 cubes, 19 of them edge cubes):
+    each kind of edge cube (padded along t, h or w, or several) first, in the middle and last,
+    and k = 1, 2, 3, so that the masked key slots of the first tile, of later tiles and of the
+    last tile are all exercised; every output row is compared with the oracle."""
+    import torch
+    wl = synth.small_workload("vsa_edge_plans", 1, 2, 9, 10, 11, 128, structured=True, seed=23, topk=3)
+    log(f"vsa fine, plan {plan} for every query cube, grid 9x10x11")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    C = g["idx"].shape[2]
+    pl = np.broadcast_to(np.array(plan, np.int32), (1, 2, C, len(plan))).copy()
+    o = torch.full((1, 2, wl.N, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((1, 2, wl.N), float("nan"), dtype=torch.float32, device="cuda")
+    o, lse = wf.wf_vsa_fine(g["ws"], torch.from_numpy(pl).cuda(), (1, 2, wl.N, 128), (wl.T, wl.H, wl.W),
+                            out=o, lse=lse)
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    tok = oracle.cube_layout(wl.T, wl.H, wl.W)
+    for h in range(2):
+        ref, lref = oracle.fine(synth.bits_to_f64(q[0, h]), synth.bits_to_f64(k[0, h]),
+                                synth.bits_to_f64(v[0, h]), tok, pl[0, h], wl.scale)
+        assert_close(o[0, h], ref, f"plan {plan} head {h}")
+        assert np.abs(lse[0, h] - lref).max() <= LSE_MAX_ABS, f"plan {plan} head {h}: lse"
+
+
 def test_vsa_error_paths(wf):
     import torch
     wl = synth.small_workload("vsa_err", 1, 1, 5, 6, 7, 128, seed=24)

@@ -493,19 +493,108 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
 }
 
 // ---------------------------------------------------------------- fine stage
+// P V of the previous tile interleaved with the probabilities of the current
+// one (p = 2^(s*sl2 - m) in bf16, as tile_probs): step i computes probability
+// pair i (two exp2, one convert) and adds it to this lane's sum, then issues
+// P V MFMA i, whose V^T operand was read kRingPF steps ahead.  The softmax's
+// VALU work thus issues while the matrix pipe runs.  Registers an MFMA reads
+// must not be rewritten while it may still read them, so every operand stays
+// live until the last MFMA has been issued (the P groups are built once,
+// before the first MFMA; each ring slot is refilled at the start of the step
+// after the one that consumed it, before any VALU work), and the function
+// ends by reading the last MFMA's result, which waits for the matrix pipe to
+// drain before any later instruction may reuse those registers.  Returns the
+// lane's sum of the new probabilities, summed in tile_probs' order.
+template <int D>
+__device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_old, f32x16* o, const f32x16& s0,
+                                               const f32x16& s1, float sl2, float m, bf16x2* p_new, int j,
+                                               int half) {
+  constexpr int NPV = Pairs<D>::NPV, PF = kRingPF, R = kRing;
+  static_assert(NPV == 16 && D == 128, "one probability pair per P V MFMA");
+  OperandBase<D> ob(j, half);
+  asm volatile("" : "+v"(ob.k), "+v"(ob.v));
+  bf16x8 pg[4];  // B operand of the k-step ks: probabilities 4 ks .. 4 ks + 3
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    pg[g] = __builtin_bit_cast(bf16x8, P4{p_old[4 * g], p_old[4 * g + 1], p_old[4 * g + 2], p_old[4 * g + 3]});
+  uint4 ring[R];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D>(u, vt, nullptr, ob);
+  const float nm = -m;
+  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+  float la = 0.f, lb = 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    if (i + PF < NPV) ring[(i + PF) % R] = mfma_operand<D>(i + PF, vt, nullptr, ob);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x16& sv = i < 8 ? s0 : s1;
+    const int r = i % 8;
+    p_new[i] = __builtin_convertvector((f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * r], sl2, nm)),
+                                               __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * r + 1], sl2, nm))},
+                                       bf16x2);
+    if (i % 2 == 0) la = __builtin_amdgcn_fdot2_f32_bf16(p_new[i], one2, la, false);
+    else lb = __builtin_amdgcn_fdot2_f32_bf16(p_new[i], one2, lb, false);
+    __builtin_amdgcn_sched_barrier(0);
+    const int ks = i / 4, b = i % 4;  // mfma_pair's numbering of the P V pairs
+    o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ring[i % R]), pg[ks], o[b], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  auto v4 = [](auto x) __attribute__((always_inline)) { return __builtin_bit_cast(i32x4, x); };
+  asm volatile("" ::"v"(v4(pg[0])), "v"(v4(pg[1])), "v"(v4(pg[2])), "v"(v4(pg[3])), "v"(v4(ring[0])),
+               "v"(v4(ring[1])), "v"(v4(ring[2])), "v"(v4(ring[3])), "v"(v4(ring[4])));
+  __builtin_amdgcn_sched_barrier(0);
+  // o[3] is the last MFMA's accumulator: reading it waits for the pipe (0 * o adds nothing to a
+  // finite sum; a non-finite O turns the sum into NaN, which only sends the caller to its
+  // recompute path)
+  return __builtin_fmaf(o[3][15], 0.f, la) + lb;
+}
+
+// softmax_tile for tile t with P(t-1) V(t-1) run inside it (pv_with_probs).
+// The arithmetic is softmax_tile's, in the same order relative to O: P V of
+// tile t-1 is accumulated before O is rescaled for tile t's reference.
+template <int D, int SM>
+__device__ __forceinline__ void softmax_tile_pv(const char* vt, const bf16x2* p_old, const f32x16& s0,
+                                                const f32x16& s1, float sl2, float& m, float& l, f32x16* o,
+                                                bf16x2* p_new, int j, int half) {
+  constexpr int DB = D / 32;
+  if constexpr (SM == kSoftmaxRunningMax) {
+    const float mnew = fmaxf(m, tile_row_max(s0, s1, sl2));
+    const float lt = pv_with_probs<D>(vt, p_old, o, s0, s1, sl2, mnew, p_new, j, half);
+    rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
+    m = mnew;
+    l += lt;
+  } else if constexpr (SM == kSoftmaxFixedFirst) {
+    l += pv_with_probs<D>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
+  } else {
+    float lt = pv_with_probs<D>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
+    if (__ballot(!(lt <= 0x1p16f))) {  // a big jump (the first tile is not run here)
+      const float mnew = fmaxf(m, ceilf(tile_row_max(s0, s1, sl2)));
+      rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
+      m = mnew;
+      lt = tile_probs(s0, s1, sl2, m, p_new);
+    }
+    l += lt;
+  }
+}
+
 // One workgroup (2 wavefronts x 32 query slots) per (bh, query cube); it walks
 // the k selected key cubes, one cube (64 keys) per tile.  K and V^T of the
-// current cube sit in one K slot and one V slot of LDS (32 KiB, so several
-// workgroups share a CU and hide each other's latency).  The slots have
-// separate lifetimes: the copy of the next K cube starts as soon as both
-// wavefronts have their scores and is waited for at the next tile's start; the
-// copy of the next V cube starts once both have accumulated P V and is waited
-// for only before the next P V, so it lands behind the next tile's scores and
-// softmax.  Padded key slots of edge cubes are masked; output rows are
-// scattered back to grid order, padded query slots are not written.  With
-// GATED the epilogue adds gate * Oc of the query cube (gated merge).  SM
-// selects the softmax reference policy (softmax_tile).  BLK is the shape of
-// the 64-token blocks (VSA's cubes; sliding-tile attention's slabs).
+// current cubes sit in one K slot and one V slot of LDS (32 KiB per
+// workgroup).  Each wavefront's tile t is: the scores S(t) = K(t) Q^T, then
+// the probabilities of tile t with P(t-1) V(t-1) interleaved (the matrix pipe
+// works through the softmax), so the P V of a tile runs one tile late and the
+// last one after the loop.  Two barriers per tile: after the scores (K slot
+// free, V(t-1) visible: the copy of K(t+1) starts and has the softmax to
+// land) and after the softmax (V slot free, K(t+1) visible: the copy of V(t)
+// starts and has the next scores to land).  Padded key slots of edge cubes
+// are masked; output rows are scattered back to grid order, padded query
+// slots are not written.  With GATED the epilogue adds gate * Oc of the
+// query cube (gated merge); the last tile loads the gate rows where other
+// tiles copy the next K cube.  SM selects the softmax reference policy
+// (softmax_tile).  BLK is the shape of the 64-token blocks (VSA's cubes;
+// sliding-tile attention's slabs).
 template <int D, bool GATED, int SM = kSoftmaxGuarded, class BLK = Cube>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
@@ -536,15 +625,15 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float m = -INFINITY, l = 0.f;
   f32x16 s0, s1;
-  bf16x2 p2[16];
+  bf16x2 pa[16], pb[16];  // P of the tile whose P V is pending, and of the tile being scored
 
-  int cur = plan[0];
   const CopyOffsets<D, 2> coff(wave, lane, 64);
-  constexpr int KP = CopyOffsets<D, 2>::KPW, VP = CopyOffsets<D, 2>::VPW;  // copies per wavefront and tile
+  constexpr int VP = CopyOffsets<D, 2>::VPW;  // V^T copies per wavefront and tile
   // the head's cube-ordered K and V^T: every copy is range-checked against these C cubes, so a
   // plan entry outside [0, C) reads zeros (cube_copy) instead of memory beyond them
   const uint16_t* khead = kc + cube_base * 64 * D;
   const uint16_t* vhead = vct + cube_base * D * 64;
+  int cur = plan[0];
   cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, cur, g.C, wave);
   cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cur, g.C, wave);
   wait_tile_copies_keep<VP>();  // K(0) landed; V(0) may still fly
@@ -552,53 +641,68 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   cube_coords(g, c, ct, ch, cw);
   const long head_row0 = (long)bh * g.T * g.H * g.W;
   GatePre gp;
-  // One tile.  LAST (the gated kernel's final tile, peeled off the loop) issues no copies of a next
-  // cube; instead, once the scores are done and Q is no longer needed, it loads the gate rows and
-  // the coarse output for the epilogue, so their latency hides behind the softmax.
-  auto tile = [&](int t, auto last_c) __attribute__((always_inline)) {
-    constexpr bool LAST = decltype(last_c)::value;
-    barrier_nofence();  // K(t) visible
-    mfma_run<D, NPV, NPV + NQK>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
-    barrier_nofence();                                                     // K slot free
-    const int nxt = t + 1 < k ? plan[t + 1] : cur;  // past the end: a harmless copy of the last cube
-    if constexpr (LAST) {
-      gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
-    } else {
-      cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, nxt, g.C, wave);
-    }
+  // masks the padded key slots of an edge block.  Each score is rewritten through a select that
+  // reads it: a plain store of -inf into an MFMA result register is a write-after-write the
+  // hardware does not order against the MFMA's own late write-back, while a read waits for it.
+  auto mask_keys = [&](int cube) __attribute__((always_inline)) {
     int kt, kh, kw;
-    cube_coords(g, cur, kt, kh, kw);
+    cube_coords(g, cube, kt, kh, kw);
     const int lt = g.T - BLK::BT * kt, lh = g.H - BLK::BH * kh, lw = g.W - BLK::BW * kw;
-    if (lt < BLK::BT || lh < BLK::BH || lw < BLK::BW) {  // edge block: mask padded key slots
+    if (lt < BLK::BT || lh < BLK::BH || lw < BLK::BW) {
       constexpr int PL = BLK::BH * BLK::BW;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int a = key_row(0, r, half), b = key_row(1, r, half);
-        if (!(a / PL < lt && (a / BLK::BW) % BLK::BH < lh && a % BLK::BW < lw)) s0[r] = -INFINITY;
-        if (!(b / PL < lt && (b / BLK::BW) % BLK::BH < lh && b % BLK::BW < lw)) s1[r] = -INFINITY;
+        const bool ra = a / PL < lt && (a / BLK::BW) % BLK::BH < lh && a % BLK::BW < lw;
+        const bool rb = b / PL < lt && (b / BLK::BW) % BLK::BH < lh && b % BLK::BW < lw;
+        s0[r] = ra ? s0[r] : -INFINITY;
+        s1[r] = rb ? s1[r] : -INFINITY;
       }
     }
-    softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, p2);
+  };
+  // tile 0: scores and probabilities (its P V runs inside tile 1's softmax)
+  barrier_nofence();                                                     // K(0) visible
+  mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // S = K(0) Q^T
+  barrier_nofence();                                                     // K slot free
+  if (k > 1) cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, plan[1], g.C, wave);
+  mask_keys(cur);
+  softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, pa);
+  wait_tile_copies();  // K(1) and V(0) landed
+  barrier_nofence();   // K(1), V(0) visible
+  // tile t >= 1.  LAST (the gated kernel's final tile, peeled off the loop so that the gate
+  // registers are live only there) loads the gate rows and the coarse output for the epilogue
+  // where other tiles copy the next K cube, so their latency hides behind the softmax.
+  auto tile = [&](int t, auto last_c) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_c)::value;
+    cur = plan[t];
+    mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
+    wait_tile_copies();  // V(t-1) landed
+    barrier_nofence();   // K slot free; V(t-1) visible
     if constexpr (LAST)
-      wait_tile_copies();          // V(t) landed, and the gate rows
-    else
-      wait_tile_copies_keep<KP>();  // V(t) landed (it had the scores and the softmax to do so); K(t+1) may fly
-    barrier_nofence();            // V(t) visible
-    mfma_run<D, 0, NPV>(vs, ks, p2, qop, oacc, s0, s1, j, half);  // O += P V(t)
-    barrier_nofence();                                             // V slot free
-    if constexpr (!LAST) {
-      cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, nxt, g.C, wave);
-      wait_tile_copies_keep<VP>();  // K(t+1) landed; V(t+1) may fly
-    }
-    cur = nxt;
+      gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
+    else if (t + 1 < k)
+      cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, plan[t + 1], g.C, wave);
+    mask_keys(cur);
+    softmax_tile_pv<D, SM>(vs, pa, s0, s1, sl2, m, l, oacc, pb, j, half);  // O += P(t-1) V(t-1); P(t)
+    wait_tile_copies();  // K(t+1) landed (or the gate rows)
+    barrier_nofence();   // V slot free; K(t+1) visible
+    cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cur, g.C, wave);  // V(t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pa[i] = pb[i];
   };
   if constexpr (GATED) {
-    for (int t = 0; t < k - 1; ++t) tile(t, std::false_type());
-    tile(k - 1, std::true_type());
+    for (int t = 1; t < k - 1; ++t) tile(t, std::false_type());
+    if (k > 1) tile(k - 1, std::true_type());
   } else {
-    for (int t = 0; t < k; ++t) tile(t, std::false_type());
+    for (int t = 1; t < k; ++t) tile(t, std::false_type());
   }
-  wait_tile_copies();  // this wavefront's copies (the last ones are redundant) have landed
+  wait_tile_copies();  // V(k-1) landed
+  barrier_nofence();   // V(k-1) visible
+  if constexpr (GATED) {  // a single tile had no later tile to load them in
+    if (k == 1) gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
+  }
+  mfma_run<D, 0, NPV>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // O += P(k-1) V(k-1)
+  wait_tile_copies();  // the gate rows (k = 1)
   barrier_nofence();   // every wavefront is done with both slots
   const float lt = l + __shfl_xor(l, 32);
   fine_epilogue<D, GATED, BLK>(oacc, 1.f / lt, wave == 0 ? ks : vs, j, half, g, ct, ch, cw, wave, head_row0, o, gp);
