@@ -150,10 +150,12 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     mfma_prefill<D, 0>(ring, vnext, kcur, j, half);  // first operands of MFMA phase t+1: V(t) rows
     if (t < nt) {
       if ((t + 1) * 64 > N) {  // ragged last tile: keys >= N do not exist
+        // selects that read the scores: a plain store into an MFMA result register is not
+        // ordered against the MFMA's own write-back, a read waits for it
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (t * 64 + key_row(0, r, half) >= N) s0[r] = -INFINITY;
-          if (t * 64 + key_row(1, r, half) >= N) s1[r] = -INFINITY;
+          s0[r] = t * 64 + key_row(0, r, half) < N ? s0[r] : -INFINITY;
+          s1[r] = t * 64 + key_row(1, r, half) < N ? s1[r] : -INFINITY;
         }
       }
       softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, p2);

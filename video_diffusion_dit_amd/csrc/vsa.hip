@@ -297,13 +297,20 @@ __global__ void __launch_bounds__(256) wf_vsa_topk(const float* __restrict__ s,
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
   if (lane == 0) stat[row] = make_float2(ml, 1.f / sum);
+  // thr ends as the k-th largest key, or -- when some candidate has exactly k keys at or above
+  // it, which usually happens long before bit 0 -- as that candidate minus one, so that the keys
+  // above thr are exactly the k largest and no tie is left to resolve (the same set either way)
   uint32_t thr = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = thr | (1u << b);
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
-    if (cnt >= k) thr = cand;
+    if (cnt == k) {
+      thr = cand - 1u;
+      break;
+    }
+    if (cnt > k) thr = cand;
   }
   int ngt = 0;
 #pragma unroll
