@@ -136,13 +136,16 @@ def vsa_bytes(wl, C) -> dict:
     Np, Cs = 64 * C, (C + 31) // 32 * 32
     BH = wl.B * wl.Hh
     gather = BH * (3 * wl.N * wl.D * 2 + 3 * Np * wl.D * 2 + 2 * C * wl.D * 4 + 2 * wl.D * Cs * 2)
+    # the one-call path's gather writes only V^T (and the means), not cube-ordered Q and K
+    gather_one_call = BH * (3 * wl.N * wl.D * 2 + Np * wl.D * 2 + 2 * C * wl.D * 4 + 2 * wl.D * Cs * 2)
     scores = BH * (2 * C * wl.D * 4 + C * Cs * 4)
     topk = BH * (C * C * 4 + C * wl.topk * 4 + C * 8)
     # coarse-branch output: scores + row statistics + hi/lo cube means of V in, O_coarse out
     coarse_out = BH * (C * Cs * 4 + C * 8 + 2 * wl.D * Cs * 2 + C * wl.D * 4)
     # the gated merge adds the gate (bf16, every real token) to the fine stage's traffic
     merge = BH * wl.N * wl.D * 2
-    return dict(gather=gather, scores=scores, topk=topk, coarse_out=coarse_out, merge=merge)
+    return dict(gather=gather, gather_one_call=gather_one_call, scores=scores, topk=topk, coarse_out=coarse_out,
+                merge=merge)
 
 
 def blas_info() -> dict:
@@ -353,18 +356,16 @@ def main():
     grid = (wv.T, wv.H, wv.W)
 
     def step(ev=None):
-        # ev: four events recorded on the launch stream around the step's three calls
+        # ev: three events recorded on the launch stream around the step's two calls; the VSA call is
+        # the one-call path (wf_vsa: coarse and fine stage, no cube-ordered copies of Q and K)
         if ev:
             ev[0].record()
         wf.wf_attn_dense(qd, kd, vd, out=od, workspace=ws_d)
         if ev:
             ev[1].record()
-        wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
+        wf.wf_vsa(qv, kv, vv, grid, wv.topk, idx=idx, out=ov, workspace=ws_v)
         if ev:
             ev[2].record()
-        wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
-        if ev:
-            ev[3].record()
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -379,7 +380,7 @@ def main():
     wf.profile_enable(True)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
@@ -389,8 +390,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
     # per-call medians over the timed steps (the means come from the library's per-kernel events)
-    per_call = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(3)] for ev in call_ev])
-    med_dense, med_coarse, med_fine = (float(np.median(per_call[:, j])) for j in range(3))
+    per_call = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(2)] for ev in call_ev])
+    med_dense, med_vsa = (float(np.median(per_call[:, j])) for j in range(2))
     kern = {}
     for name in ("wf_transpose_v", "wf_dense_fwd", "wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk",
                  "wf_vsa_fine"):
@@ -400,36 +401,45 @@ def main():
 
     dense_tf_step = dense_flops(wd) / (kern["wf_dense_fwd"] * 1e-3) / 1e12  # for dense-equivalent times
 
-    # extra record (not part of the step): VSA at the review's 78-of-624 operating point
-    k78, k78_ms = synth.WORKLOADS["vsa_480p_k78"].topk, None
-    if not args.no_extra:
-        idx78 = torch.empty((wv.B, wv.Hh, C, k78), dtype=torch.int32, device=dev)
-
-        def vsa78():
-            wf.wf_vsa_coarse_topk(qv, kv, vv, grid, k78, idx=idx78, workspace=ws_v)
-            wf.wf_vsa_fine(ws_v, idx78, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
-
-        vsa78()
+    def vsa_kernel_ms(fn, reps):
+        fn()
         torch.cuda.synchronize()
         wf.profile_enable(True)
-        for _ in range(max(3, args.steps // 2)):
-            vsa78()
+        for _ in range(reps):
+            fn()
         torch.cuda.synchronize()
-        k78_ms = {}
+        out_ms = {}
         for name in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine"):
             n, tot = wf.profile_query(name)
-            k78_ms[name] = tot / n
+            out_ms[name] = tot / n
         wf.profile_enable(False)
+        return out_ms
+
+    # extra records (not part of the step): the same VSA call through the two-call path
+    # (wf_vsa_coarse_topk + wf_vsa_fine, with cube-ordered copies of Q and K), and both paths at
+    # the review's 78-of-624 operating point
+    k78, k78_ms, k78_two_ms, two_ms = synth.WORKLOADS["vsa_480p_k78"].topk, None, None, None
+    if not args.no_extra:
+        idx78 = torch.empty((wv.B, wv.Hh, C, k78), dtype=torch.int32, device=dev)
+        reps = max(3, args.steps // 2)
+
+        def two_calls(kk, ix):
+            wf.wf_vsa_coarse_topk(qv, kv, vv, grid, kk, idx=ix, workspace=ws_v)
+            wf.wf_vsa_fine(ws_v, ix, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
+
+        two_ms = vsa_kernel_ms(lambda: two_calls(wv.topk, idx), reps)
+        k78_ms = vsa_kernel_ms(lambda: wf.wf_vsa(qv, kv, vv, grid, k78, idx=idx78, out=ov, workspace=ws_v), reps)
+        k78_two_ms = vsa_kernel_ms(lambda: two_calls(k78, idx78), reps)
 
     # extra record (not part of the step): VSA with the gated merge (coarse-branch output plus
-    # gate * O_coarse added in the fine stage's epilogue), same inputs and top-k, gate ~ U[0, 1)
+    # gate * O_coarse added in the fine stage's epilogue), same inputs and top-k, gate ~ U[0, 1),
+    # through the one-call path
     gated_ms = None
     if not args.no_extra:
         gate = to_dev(synth.make_gate(wv))
 
-        def vsa_gated():
-            wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
-            wf.wf_vsa_fine_gated(ws_v, idx, gate, grid, out=ov)
+        def vsa_gated():  # the one-call path with a gate, as the step's VSA call
+            wf.wf_vsa(qv, kv, vv, grid, wv.topk, idx=idx, out=ov, workspace=ws_v, gate=gate)
 
         vsa_gated()
         torch.cuda.synchronize()
@@ -559,8 +569,7 @@ def main():
 
         def run720():
             wf.wf_attn_dense(q7, k7, v7, out=o7, workspace=wsd7)
-            wf.wf_vsa_coarse_topk(q7, k7, v7, g7, wv7.topk, idx=idx7, workspace=wsv7)
-            wf.wf_vsa_fine(wsv7, idx7, (wv7.B, wv7.Hh, wv7.N, wv7.D), g7, out=o7)
+            wf.wf_vsa(q7, k7, v7, g7, wv7.topk, idx=idx7, out=o7, workspace=wsv7)
 
         run720()
         torch.cuda.synchronize()
@@ -601,8 +610,7 @@ def main():
 
         def step_share():
             wf.wf_attn_dense(qs, ks_, vs_, out=os_, workspace=ws_s)
-            wf.wf_vsa_coarse_topk(qvs, kvs, vvs, grid, wv.topk, idx=idxs, workspace=ws_vs)
-            wf.wf_vsa_fine(ws_vs, idxs, (wv.B, hs, wv.N, wv.D), grid, out=ovs)
+            wf.wf_vsa(qvs, kvs, vvs, grid, wv.topk, idx=idxs, out=ovs, workspace=ws_vs)
 
         for _ in range(3):
             step_share()
@@ -675,17 +683,18 @@ def main():
             "algorithmic_tflop": fl_d / 1e12,
         },
         "vsa": {
+            "path": "one call (wf_vsa): the gather writes V^T and the cube means only, the fine stage reads Q and K "
+                    "from the token grid",
             "ms_per_call": ms_vsa,
-            "ms_per_call_median": med_coarse + med_fine,
-            "coarse_call_ms_median": med_coarse,
-            "fine_call_ms_median": med_fine,
+            "ms_per_call_median": med_vsa,
+            "coarse_ms": kern["wf_vsa_gather"] + kern["wf_vsa_scores"] + kern["wf_vsa_topk"],
             "kernel_ms": {k: kern[k] for k in ("wf_vsa_gather", "wf_vsa_scores", "wf_vsa_topk", "wf_vsa_fine")},
             "fine_tflops": fl_v["fine"] / (kern["wf_vsa_fine"] * 1e-3) / 1e12,
             "fine_tflops_padded_queries": fl_v["fine"] * C * 64 / wv.N / (kern["wf_vsa_fine"] * 1e-3) / 1e12,
             "fine_frac_bf16_peak": fl_v["fine"] / (kern["wf_vsa_fine"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "gather_gbs": by_v["gather"] / (kern["wf_vsa_gather"] * 1e-3) / 1e9,
+            "gather_gbs": by_v["gather_one_call"] / (kern["wf_vsa_gather"] * 1e-3) / 1e9,
             "topk_gbs": by_v["topk"] / (kern["wf_vsa_topk"] * 1e-3) / 1e9,
-            "gather_frac_hbm": by_v["gather"] / (kern["wf_vsa_gather"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "gather_frac_hbm": by_v["gather_one_call"] / (kern["wf_vsa_gather"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "topk_frac_hbm": by_v["topk"] / (kern["wf_vsa_topk"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "scores_gbs": by_v["scores"] / (kern["wf_vsa_scores"] * 1e-3) / 1e9,
             "dense_equivalent_speedup": ms_dense_same / ms_vsa,
@@ -706,6 +715,13 @@ def main():
         "sta": sta,
         "rope": rope,
         "softmax_policies": policies,
+        "vsa_two_calls": None if two_ms is None else {
+            "topk": wv.topk,
+            "ms_per_call": sum(two_ms.values()),
+            "kernel_ms": two_ms,
+            "gather_gbs": by_v["gather"] / (two_ms["wf_vsa_gather"] * 1e-3) / 1e9,
+            "fine_tflops": fl_v["fine"] / (two_ms["wf_vsa_fine"] * 1e-3) / 1e12,
+        },
         "vsa_k78": None if k78_ms is None else {
             "topk": k78,
             "ms_per_call": sum(k78_ms.values()),
@@ -713,6 +729,12 @@ def main():
             "fine_tflops_page_convention": 4.0 * wv.N * 64 * k78 * wv.D * wv.Hh / (k78_ms["wf_vsa_fine"] * 1e-3) / 1e12,
             "dense_equivalent_speedup": ms_dense_same / sum(k78_ms.values()),
             "ideal_speedup": ideal_speedup(synth.WORKLOADS["vsa_480p_k78"], C),
+            "two_calls": {
+                "ms_per_call": sum(k78_two_ms.values()),
+                "kernel_ms": k78_two_ms,
+                "fine_tflops_page_convention": (4.0 * wv.N * 64 * k78 * wv.D * wv.Hh
+                                                / (k78_two_ms["wf_vsa_fine"] * 1e-3) / 1e12),
+            },
         },
         "per_gpu_share": share,
         "context": {"pages_dense_ms_b200": 17.0,

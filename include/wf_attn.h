@@ -182,6 +182,29 @@ int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t
                     float scale, int32_t topk, float* o, float* lse, void* stream);
 
 /*
+ * VSA in one call: the coarse stage and the fine stage of wf_vsa_coarse_topk
+ * followed by wf_vsa_fine (or, with a gate, wf_vsa_fine_gated) on the plan it
+ * selects, with the same result (o, lse, idx and o_coarse bit for bit).  The
+ * one call needs no cube-ordered copies of Q and K: the fine stage reads them
+ * from q and k in grid order, so the gather moves about a third fewer bytes.
+ *
+ *   q, k, v        bf16 [B][Hh][T*H*W][D], read only; D must be 128.
+ *   topk           1 <= topk <= C.
+ *   idx            int32 [B][Hh][C][topk], written (the plan, as wf_vsa_coarse_topk).
+ *   gate           bf16 [B][Hh][T*H*W][D] or NULL: with a gate the call adds the
+ *                  gated coarse branch, o = o_fine + gate * Oc, as wf_vsa_fine_gated.
+ *   o, lse         as for wf_vsa_fine (lse may be NULL).
+ *   o_coarse       fp32 [B][Hh][C][D]: Oc, written; may be NULL, and must be
+ *                  NULL without a gate.
+ *   workspace      at least wf_vsa_workspace_bytes(); its contents afterwards
+ *                  are not a workspace that wf_vsa_fine or wf_vsa_fine_gated
+ *                  can take (the cube-ordered Q and K are not written).
+ */
+int32_t wf_vsa(const void* q, const void* k, const void* v, int32_t B, int32_t Hh, int32_t T, int32_t H,
+               int32_t W, int32_t D, float scale, int32_t topk, int32_t* idx, const void* gate, float* o,
+               float* lse, float* o_coarse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * VSA fine stage with the gated merge ("VSA selects cubes", part 3: the fine
  * result is kept whole and a learned share of the coarse branch is added).
  * The coarse branch's output for query cube c is the cube-level attention of

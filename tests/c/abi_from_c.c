@@ -19,7 +19,7 @@ static int failures = 0;
 int main(void) {
   char buf[64];
   void* const fake = (void*)(size_t)0x10000; /* aligned, never dereferenced */
-  EXPECT(wf_abi_version() == 3);
+  EXPECT(wf_abi_version() == 4);
   EXPECT(strcmp(wf_status_string(WF_OK), "WF_OK") == 0);
   EXPECT(strcmp(wf_status_string(WF_ERR_WORKSPACE), "WF_ERR_WORKSPACE") == 0);
   EXPECT(wf_vsa_num_cubes(21, 30, 52) == 624);
@@ -41,6 +41,8 @@ int main(void) {
                             NULL) == WF_ERR_INVALID_ARG);
   EXPECT(wf_vsa_fine(fake, 16, (const int32_t*)fake, 1, 2, 5, 6, 7, 128, 0.1f, 2, (float*)fake, NULL, NULL) ==
          WF_ERR_WORKSPACE);
+  EXPECT(wf_vsa(fake, fake, fake, 1, 2, 5, 6, 7, 128, 0.1f, 3, (int32_t*)fake, NULL, NULL, NULL, NULL, fake,
+                1u << 30, NULL) == WF_ERR_INVALID_ARG);
   EXPECT(wf_rope_qk(fake, fake, fake, fake, 1, 2, 5, 6, 7, 128, 1e4, 16, NULL) == WF_ERR_INVALID_ARG);
   EXPECT(wf_sta(fake, fake, fake, 1, 2, 5, 6, 7, 128, 0.1f, 1, 1, 1, (float*)fake, NULL, NULL, fake, 1u << 30,
                 NULL) == WF_ERR_UNSUPPORTED);

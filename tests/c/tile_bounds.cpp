@@ -3,7 +3,10 @@
 //  * in the fine stage a key cube inside [0, C) is read only from its own 16 KiB, and an
 //    index outside [0, C) -- any int, including ones whose byte offset would wrap 32 bits --
 //    gets a per-lane offset at or past the end of the head's region, which the buffer
-//    descriptor's range check turns into zeros.
+//    descriptor's range check turns into zeros;
+//  * the one-call path's K copy from the token grid (wf_grid.hpp) reads, for every real slot of
+//    every cube of ragged and even grids, exactly the bytes the cube-ordered copy reads for it,
+//    and for a cube index outside [0, C) starts at the head's end.
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -11,6 +14,7 @@
 #include <climits>
 #include <vector>
 
+#include "wf_grid.hpp"
 #include "wf_tiles.hpp"
 
 static int fails = 0;
@@ -78,11 +82,42 @@ static void fine_bounds(int C) {
   }
 }
 
+static void grid_copy(int T, int H, int W) {
+  const int nt = (T + 3) / 4, nh = (H + 3) / 4, nw = (W + 3) / 4, C = nt * nh * nw;
+  const uint32_t N = (uint32_t)T * H * W;
+  for (int cube = -2; cube < C + 2; ++cube) {
+    const bool valid = cube >= 0 && cube < C;
+    const uint32_t first = wf::cube_first_token(cube, C, nh, nw, H, W, N);
+    if (!valid) {
+      EXPECT(first == N, "grid %dx%dx%d: bad cube %d starts at token %u, not the end %u\n", T, H, W, cube, first, N);
+      continue;
+    }
+    const int ct = cube / (nw * nh), ch = (cube / nw) % nh, cw = cube % nw;
+    for (int i = 0; i < 8; ++i)
+      for (int w = 0; w < 2; ++w)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int slot = 4 * (2 * i + w) + lane / 16;
+          const int t = 4 * ct + slot / 16, h = 4 * ch + (slot / 4) % 4, x = 4 * cw + slot % 4;
+          const uint64_t off = wf::grid_k_offset(first, i, w, lane, H, W);
+          EXPECT(off < (1ull << 31), "grid %dx%dx%d cube %d: offset %llu does not fit\n", T, H, W, cube,
+                 (unsigned long long)off);
+          if (t < T && h < H && x < W) {  // a real slot: the bytes the cube-ordered copy reads for it
+            const uint64_t tok = ((uint64_t)t * H + h) * W + x;
+            const uint64_t want = tok * 256 + (uint64_t)wf::Swz<128>::kslot(slot, lane % 16) * 16;
+            EXPECT(off == want, "grid %dx%dx%d cube %d piece %d w %d lane %d: %llu, want %llu\n", T, H, W, cube, i,
+                   w, lane, (unsigned long long)off, (unsigned long long)want);
+          }
+        }
+  }
+}
+
 int main() {
   coverage<128, 2>();
   coverage<128, 4>();
   coverage<64, 4>();
   for (int C : {1, 8, 27, 624, 1200, 1296, 1440, 4096}) fine_bounds(C);
+  const int grids[][3] = {{1, 1, 1}, {4, 4, 4}, {5, 6, 7}, {9, 10, 11}, {21, 30, 52}, {21, 45, 80}, {13, 6, 21}};
+  for (const auto& gr : grids) grid_copy(gr[0], gr[1], gr[2]);
   if (fails) {
     printf("%d failures\n", fails);
     return 1;

@@ -25,7 +25,7 @@ def wf():
 def test_every_declared_symbol_is_exported(wf):
     names = declared_functions()
     assert "wf_attn_dense" in names and "wf_vsa_coarse_topk" in names and "wf_vsa_fine" in names
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(wf.lib, n), f"{n} declared in wf_attn.h but not exported"
 
@@ -34,7 +34,7 @@ def test_status_strings(wf):
     assert wf.lib.wf_status_string(0) == b"WF_OK"
     assert wf.lib.wf_status_string(4) == b"WF_ERR_BAD_INDEX"
     assert wf.lib.wf_status_string(99) == b"WF_UNKNOWN_STATUS"
-    assert wf.lib.wf_abi_version() == 3
+    assert wf.lib.wf_abi_version() == 4
 
 
 def test_geometry_queries(wf):
@@ -117,6 +117,17 @@ def test_vsa_argument_errors(wf):
     assert fine(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 0, FAKE, None, None) == 1
     assert fine(FAKE, 10, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None) == 3
     assert fine(FAKE, 1 << 30, FAKE, 1, 2, 5, 6, 7, 128, float("inf"), 3, FAKE, None, None) == 1
+    one = wf.lib.wf_vsa  # the one-call path: the coarse stage's checks, plus o, gate and o_coarse
+    assert one(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, None, None, None, FAKE, 1 << 30, None) == 1
+    assert one(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 9, FAKE, None, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    assert one(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 64, 0.1, 3, FAKE, None, FAKE, None, None, FAKE, 1 << 30, None) == 2
+    assert one(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, FAKE, None, None, FAKE, 100, None) == 3
+    assert one(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, FAKE, FAKE + 2, None, FAKE, 1 << 30,
+               None) == 1
+    assert one(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert b"o_coarse given without a gate" in wf.lib.wf_last_error_detail()
+    assert one(FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.1, 3, FAKE, FAKE + 2, FAKE, None, None, FAKE, 1 << 30,
+               None) == 1
     rope = wf.lib.wf_rope_qk
     assert rope(FAKE, FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 128, 0.0, 32, None) == 1
     assert rope(FAKE, FAKE, FAKE, FAKE, 1, 2, 5, 6, 7, 96, 1e4, 32, None) == 2

@@ -56,18 +56,21 @@ def buffers(wf, q):
         o_fine=torch.empty((B, Hh, N, D), **f32), lse_fine=torch.empty((B, Hh, N), **f32),
         o_gated=torch.empty((B, Hh, N, D), **f32), o_coarse=torch.empty((B, Hh, C, D), **f32),
         o_sta=torch.empty((1, 1, Ns, D), **f32),
+        idx_one=torch.empty((B, Hh, C, TOPK), dtype=torch.int32, device=q.device),
+        o_one=torch.empty((B, Hh, N, D), **f32), lse_one=torch.empty((B, Hh, N), **f32),
         ws_dense=torch.empty(wf.dense_workspace_bytes(B, Hh, N, D), dtype=torch.uint8, device=q.device),
         ws_vsa=torch.empty(wf.vsa_workspace_bytes(B, Hh, T, H, W, D), dtype=torch.uint8, device=q.device),
+        ws_one=torch.empty(wf.vsa_workspace_bytes(B, Hh, T, H, W, D), dtype=torch.uint8, device=q.device),
         ws_sta=torch.empty(ws_sta, dtype=torch.uint8, device=q.device),
     )
 
 
 OUTPUTS = ("o_dense", "lse_dense", "q_rot", "k_rot", "idx", "scores", "o_fine", "lse_fine", "o_gated",
-           "o_coarse", "o_sta")
+           "o_coarse", "o_sta", "idx_one", "o_one", "lse_one")
 
 
 def path(wf, q, k, v, gate, sta_qkv, b):
-    """The whole path once: dense, RoPE, VSA coarse (RoPE fused) + fine + gated, STA."""
+    """The whole path once: dense, RoPE, VSA coarse (RoPE fused) + fine + gated, STA, VSA in one call."""
     wf.wf_attn_dense(q, k, v, out=b["o_dense"], lse=b["lse_dense"], workspace=b["ws_dense"])
     wf.wf_rope_qk(q, k, GRID, q_out=b["q_rot"], k_out=b["k_rot"])
     wf.wf_vsa_coarse_topk(q, k, v, GRID, TOPK, idx=b["idx"], scores=b["scores"], workspace=b["ws_vsa"],
@@ -75,6 +78,7 @@ def path(wf, q, k, v, gate, sta_qkv, b):
     wf.wf_vsa_fine(b["ws_vsa"], b["idx"], tuple(q.shape), GRID, out=b["o_fine"], lse=b["lse_fine"])
     wf.wf_vsa_fine_gated(b["ws_vsa"], b["idx"], gate, GRID, out=b["o_gated"], o_coarse=b["o_coarse"])
     wf.wf_sta(*sta_qkv, STA_GRID, WINDOW, out=b["o_sta"], lse=None, workspace=b["ws_sta"])
+    wf.wf_vsa(q, k, v, GRID, TOPK, idx=b["idx_one"], out=b["o_one"], lse=b["lse_one"], workspace=b["ws_one"])
 
 
 def poison(b):

@@ -230,6 +230,47 @@ def test_vsa_fine_edge_cube_plans(wf, plan):
         assert np.abs(lse[0, h] - lref).max() <= LSE_MAX_ABS, f"plan {plan} head {h}: lse"
 
 
+@pytest.mark.parametrize("grid,topk,B,Hh", [((5, 6, 7), 3, 1, 2), ((9, 10, 11), 5, 2, 1), ((1, 1, 1), 1, 1, 1),
+                                            ((13, 6, 21), 17, 1, 2), ((21, 30, 52), 32, 1, 3)])
+def test_vsa_one_call_equals_two_calls(wf, grid, topk, B, Hh):
+    """wf_vsa (no cube-ordered copies of Q and K; the fine stage reads them from the token grid)
+    gives the plan, O and lse of wf_vsa_coarse_topk + wf_vsa_fine bit for bit, and O matches the
+    oracle's fine stage on that plan."""
+    import torch
+    T, H, W = grid
+    wl = synth.small_workload("vsa_one_call", B, Hh, T, H, W, 128, structured=True, seed=T * 7 + topk, topk=topk)
+    log(f"vsa one call grid={grid} topk={topk} B={B} Hh={Hh}")
+    q, k, v = synth.make_qkv(wl)
+    g = gpu_vsa(wf, wl, q, k, v)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    C = g["idx"].shape[2]
+    idx = torch.full((B, Hh, C, topk), -1, dtype=torch.int32, device="cuda")
+    o = torch.full(tuple(qd.shape), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full(tuple(qd.shape[:3]), float("nan"), dtype=torch.float32, device="cuda")
+    o, lse, idx = wf.wf_vsa(qd, kd, vd, (T, H, W), topk, idx=idx, out=o, lse=lse)
+    o, lse, idx = o.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+    assert (idx == g["idx"]).all(), "plan differs from the two-call path"
+    assert np.array_equal(o.view(np.uint32), g["o"].view(np.uint32)), "O differs from the two-call path"
+    assert np.array_equal(lse.view(np.uint32), g["lse"].view(np.uint32)), "lse differs from the two-call path"
+    # with a gate: the gated merge of wf_vsa_fine_gated on the two-call workspace, bit for bit
+    gate = to_device(synth.make_gate(wl))
+    og2, _, oc2 = wf.wf_vsa_fine_gated(g["ws"], g["idx_dev"], gate, (T, H, W), with_coarse=True)
+    oc1 = torch.full((B, Hh, C, 128), float("nan"), dtype=torch.float32, device="cuda")
+    og1 = torch.full(tuple(qd.shape), float("nan"), dtype=torch.float32, device="cuda")
+    og1, _, _ = wf.wf_vsa(qd, kd, vd, (T, H, W), topk, out=og1, gate=gate, o_coarse=oc1)
+    assert torch.equal(og1.view(torch.int32), og2.view(torch.int32)), "gated O differs from the two-call path"
+    assert torch.equal(oc1.view(torch.int32), oc2.view(torch.int32)), "O_coarse differs from the two-call path"
+    tok = oracle.cube_layout(T, H, W)
+    for b in range(B):
+        for h in range(min(Hh, 2)):
+            ref, lref = oracle.fine(synth.bits_to_f64(q[b, h]), synth.bits_to_f64(k[b, h]),
+                                    synth.bits_to_f64(v[b, h]), tok, idx[b, h], wl.scale,
+                                    None if T * H * W < 8192 else list(range(0, C, 7)))
+            m = ~np.isnan(lref)
+            assert_close(o[b, h][m], ref[m], f"one call b{b} h{h}")
+            assert errors(lse[b, h][m], lref[m])[0] <= LSE_MAX_ABS
+
+
 def test_vsa_error_paths(wf):
     import torch
     wl = synth.small_workload("vsa_err", 1, 1, 5, 6, 7, 128, seed=24)

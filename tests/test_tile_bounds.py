@@ -1,6 +1,7 @@
 """The kernels' copy offsets evaluated on the host (no GPU): full coverage of every tile
-copy, and fine-stage reads confined to the selected cube or, for a plan entry outside
-[0, C), past the end of the head's region, where the buffer range check returns zeros."""
+copy, fine-stage reads confined to the selected cube or, for a plan entry outside [0, C),
+past the end of the head's region, where the buffer range check returns zeros, and the
+one-call path's K copy from the token grid reading exactly what the cube-ordered copy reads."""
 import os
 import shutil
 import subprocess

@@ -38,6 +38,8 @@ _SIGS = {
     "wf_vsa_coarse_topk": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                   _vp, _vp, _vp, _sz, _vp]),
     "wf_vsa_fine": (_i32, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp]),
+    "wf_vsa": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp,
+                      _vp, _sz, _vp]),
     "wf_vsa_fine_gated": (_i32, [_vp, _sz, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                  _vp, _vp, _vp, _vp]),
     "wf_rope_qk": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_double, _i32,
@@ -239,6 +241,40 @@ def wf_vsa_coarse_topk(q, k, v, grid, topk: int, scale: Optional[float] = None,
                                            ws.data_ptr(), ws.numel() * ws.element_size(),
                                            _stream_handle(q.device)), "wf_vsa_coarse_topk_rope")
     return idx, scores, ws
+
+
+def wf_vsa(q, k, v, grid, topk: int, scale: Optional[float] = None, with_lse: bool = False, idx=None,
+           out=None, lse=None, workspace=None, gate=None, o_coarse=None):
+    """VSA in one call through wf_vsa (coarse stage and fine stage, no cube-ordered copies of Q and K;
+    with a gate, the gated coarse branch too).
+
+    grid = (T, H, W).  Returns (o, lse or None, idx int32 [B,Hh,C,topk]).
+    """
+    torch = _torch()
+    _qkv_check(q, k, v)
+    T, H, W = grid
+    B, Hh, N, D = q.shape
+    if N != T * H * W:
+        raise ValueError(f"N = {N} but the grid has {T * H * W} tokens")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    C = num_cubes(T, H, W)
+    if idx is None:
+        idx = torch.empty((B, Hh, C, max(topk, 1)), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hh, N, D), dtype=torch.float32, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    _expect(idx, "idx", (B, Hh, C, max(topk, 1)), torch.int32, q.device)  # topk < 1: the library says why
+    _expect(out, "out", (B, Hh, N, D), torch.float32, q.device)
+    _expect(lse, "lse", (B, Hh, N), torch.float32, q.device)
+    _expect(gate, "gate", (B, Hh, N, D), torch.bfloat16, q.device)
+    _expect(o_coarse, "o_coarse", (B, Hh, C, D), torch.float32, q.device)
+    ws = _workspace(vsa_workspace_bytes(B, Hh, T, H, W, D), q.device, workspace)
+    _expect_workspace(ws, q.device)
+    _check(lib.wf_vsa(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hh, T, H, W, D, scale, topk, idx.data_ptr(),
+                      _ptr(gate), out.data_ptr(), _ptr(lse), _ptr(o_coarse), ws.data_ptr(),
+                      ws.numel() * ws.element_size(), _stream_handle(q.device)), "wf_vsa")
+    return out, lse, idx
 
 
 def wf_vsa_fine(workspace, idx, shape, grid, scale: Optional[float] = None, with_lse: bool = False,

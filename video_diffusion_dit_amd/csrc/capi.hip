@@ -124,7 +124,7 @@ const char* wf_status_string(int32_t status) {
 
 const char* wf_last_error_detail(void) { return g_detail.c_str(); }
 
-int32_t wf_abi_version(void) { return 3; }
+int32_t wf_abi_version(void) { return 4; }
 
 size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D) {
   if (!sizes_ok(B, Hh, N, D)) return 0;
@@ -259,6 +259,34 @@ int32_t wf_vsa_coarse_topk(const void* q, const void* k, const void* v, int32_t 
                            size_t workspace_bytes, void* stream) {
   return vsa_coarse(q, k, v, B, Hh, T, H, W, D, scale, topk, 0.0, 0, idx, coarse_scores, workspace,
                     workspace_bytes, stream);
+}
+
+int32_t wf_vsa(const void* q, const void* k, const void* v, int32_t B, int32_t Hh, int32_t T, int32_t H,
+               int32_t W, int32_t D, float scale, int32_t topk, int32_t* idx, const void* gate, float* o,
+               float* lse, float* o_coarse, void* workspace, size_t workspace_bytes, void* stream) {
+  WF_CHECK_PTR(q);
+  WF_CHECK_PTR(k);
+  WF_CHECK_PTR(v);
+  WF_CHECK_PTR(idx);
+  WF_CHECK_OPT_PTR(gate);
+  WF_CHECK_PTR(o);
+  WF_CHECK_OPT_PTR(lse);
+  WF_CHECK_OPT_PTR(o_coarse);
+  if (o_coarse && !gate) return fail(WF_ERR_INVALID_ARG, "o_coarse given without a gate");
+  if (int32_t st = vsa_check_sizes(B, Hh, T, H, W, D)) return st;
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(WF_ERR_INVALID_ARG, "scale %g must be finite and > 0", (double)scale);
+  const int32_t C = wf_vsa_num_cubes(T, H, W);
+  if (topk < 1 || topk > C) return fail(WF_ERR_INVALID_ARG, "topk %d outside [1, %d]", topk, C);
+  const size_t need = wf::vsa_layout(B * Hh, T, H, W, D).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  WF_CHECK_PTR(workspace);
+  hipError_t e = wf::launch_vsa_onecall(q, k, v, B * Hh, T, H, W, D, scale, topk, idx, gate, o, lse, o_coarse,
+                                        workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "VSA launch");
+  return ok();
 }
 
 int32_t wf_vsa_coarse_topk_rope(const void* q, const void* k, const void* v, int32_t B, int32_t Hh,

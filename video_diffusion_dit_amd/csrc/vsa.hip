@@ -11,6 +11,7 @@
 
 #include "wf_attn.h"
 #include "wf_device.hpp"
+#include "wf_grid.hpp"
 #include "wf_launch.hpp"
 #include "wf_rope.hpp"
 
@@ -87,8 +88,10 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 // precision (32 or 64), 0 for none.  BLK is the block shape (VSA's cubes, or
 // sliding-tile attention's slabs, which need no means).  Q, K, V are read and
 // the copies written with the streaming (non-temporal) policy: each byte is
-// touched once here (3% faster than the default policy at 480p).
-template <int D, int ROPE, class BLK = Cube, bool POOL = true>
+// touched once here (3% faster than the default policy at 480p).  Without
+// QK_COPIES only the means of Q and K and the copy of V^T are written (the
+// one-call path's fine stage reads Q and K from the token grid).
+template <int D, int ROPE, class BLK = Cube, bool POOL = true, bool QK_COPIES = true>
 __global__ void __launch_bounds__(256) wf_vsa_gather(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ qc, uint16_t* __restrict__ kc, uint16_t* __restrict__ vct,
@@ -148,8 +151,10 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       }
       const uint16_t* e = reinterpret_cast<const uint16_t*>(&u);
       if (which < 2) {
-        uint16_t* dst = (which == 0 ? qc : kc) + (cube_row0 + s) * D + c16 * 8;
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u), reinterpret_cast<u32x4*>(dst));
+        if constexpr (QK_COPIES) {
+          uint16_t* dst = (which == 0 ? qc : kc) + (cube_row0 + s) * D + c16 * 8;
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u), reinterpret_cast<u32x4*>(dst));
+        }
       } else {
 #pragma unroll
         for (int t = 0; t < 8; ++t) vtile[s * VSTR + c16 * 8 + t] = e[t];
@@ -504,6 +509,27 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
   }
 }
 
+// ---------------------------------------------------------------- grid-order K copy
+// Copy of key cube `cube` of one head's K straight from the token grid (K [N][D], tokens in
+// row-major (t, h, w) order), for the one-call path, which skips the cube-ordered copy of K.
+// The LDS tile is the one cube_copy writes: piece i of wavefront w holds cube slots
+// 4 (2i + w) .. +3, i.e. slot row dt = (2i + w) / 4, dh = (2i + w) % 4, dw = lane / 16, 16 lanes
+// of 16 bytes per token row with the chunk swizzle of Swz.  A slot outside the grid reads some
+// other row of the head, or zeros past its end (range check); those keys are masked before the
+// softmax.  A cube index outside [0, C) starts at the head's end and reads zeros.
+template <int D>
+__device__ __forceinline__ void grid_k_copy(const uint16_t* khead, uint32_t head_bytes, char* kdst, int cube,
+                                            const Grid3& g, int w, int lane) {
+  static_assert(D == 128, "16 chunks of 16 bytes per row");
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const uint32_t first = cube_first_token(cube, g.C, g.nh, g.nw, g.H, g.W, head_bytes / (D * 2));
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(khead, head_bytes);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kdst + (i * 2 + w) * 1024), 16,
+                                             (int)grid_k_offset(first, i, w, lane, g.H, g.W), 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- fine stage
 // P V of the previous tile interleaved with the probabilities of the current
 // one (p = 2^(s*sl2 - m) in bf16, as tile_probs): step i computes probability
@@ -606,8 +632,12 @@ __device__ __forceinline__ void softmax_tile_pv(const char* vt, const bf16x2* p_
 // query cube (gated merge); the last tile loads the gate rows where other
 // tiles copy the next K cube.  SM selects the softmax reference policy
 // (softmax_tile).  BLK is the shape of the 64-token blocks (VSA's cubes;
-// sliding-tile attention's slabs).
-template <int D, bool GATED, int SM = kSoftmaxGuarded, class BLK = Cube>
+// sliding-tile attention's slabs).  With GRID_QK, qc and kc are the token-grid
+// Q and K themselves ([BH][N][D]): the query rows are loaded by token (padded
+// slots get zero rows, as in the cube-ordered copy, so the result is the same
+// bit for bit) and the K tiles are copied with grid_k_copy, so the gather need
+// not write cube-ordered copies of them.
+template <int D, bool GATED, int SM = kSoftmaxGuarded, class BLK = Cube, bool GRID_QK = false>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vct, const int* __restrict__ idx, float* __restrict__ o,
@@ -623,12 +653,26 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   const long cube_base = (long)bh * g.C;
   const int* plan = idx + bh * plan_stride + (long)c * k;  // plan_stride 0: one plan shared by all heads
   const int slot = wave * 32 + j;
+  int ct, ch, cw;
+  cube_coords(g, c, ct, ch, cw);
+  const long N = (long)g.T * g.H * g.W;
+  const long head_row0 = (long)bh * N;
 
   bf16x8 qop[D / 16];
   {
-    const uint16_t* qr = qc + ((cube_base + c) * 64 + slot) * D;
+    if constexpr (GRID_QK) {  // a padded slot gets a zero row, as in the cube-ordered copy
+      const int tq = slot_token<BLK>(g, ct, ch, cw, slot);
+      const uint16_t* qr = qc + (head_row0 + (tq >= 0 ? tq : 0)) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kk * 16 + half * 8));
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const uint4 u = *reinterpret_cast<const uint4*>(qr + kk * 16 + half * 8);
+        qop[kk] = as_bf16x8(tq >= 0 ? u : make_uint4(0, 0, 0, 0));
+      }
+    } else {
+      const uint16_t* qr = qc + ((cube_base + c) * 64 + slot) * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + kk * 16 + half * 8));
+    }
   }
   f32x16 oacc[DB];
 #pragma unroll
@@ -643,15 +687,19 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   constexpr int VP = CopyOffsets<D, 2>::VPW;  // V^T copies per wavefront and tile
   // the head's cube-ordered K and V^T: every copy is range-checked against these C cubes, so a
   // plan entry outside [0, C) reads zeros (cube_copy) instead of memory beyond them
-  const uint16_t* khead = kc + cube_base * 64 * D;
+  const uint16_t* khead = GRID_QK ? kc + head_row0 * D : kc + cube_base * 64 * D;
   const uint16_t* vhead = vct + cube_base * D * 64;
+  // the next K tile: from the cube-ordered copy, or (GRID_QK) from the token grid
+  auto copy_k = [&](int cube) __attribute__((always_inline)) {
+    if constexpr (GRID_QK)
+      grid_k_copy<D>(khead, (uint32_t)(N * D * 2), ks, cube, g, wave, lane);
+    else
+      cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, cube, g.C, wave);
+  };
   int cur = plan[0];
-  cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, cur, g.C, wave);
+  copy_k(cur);
   cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cur, g.C, wave);
   wait_tile_copies_keep<VP>();  // K(0) landed; V(0) may still fly
-  int ct, ch, cw;
-  cube_coords(g, c, ct, ch, cw);
-  const long head_row0 = (long)bh * g.T * g.H * g.W;
   GatePre gp;
   // masks the padded key slots of an edge block.  Each score is rewritten through a select that
   // reads it: a plain store of -inf into an MFMA result register is a write-after-write the
@@ -676,7 +724,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   barrier_nofence();                                                     // K(0) visible
   mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // S = K(0) Q^T
   barrier_nofence();                                                     // K slot free
-  if (k > 1) cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, plan[1], g.C, wave);
+  if (k > 1) copy_k(plan[1]);
   mask_keys(cur);
   softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, pa);
   wait_tile_copies();  // K(1) and V(0) landed
@@ -693,7 +741,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     if constexpr (LAST)
       gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
     else if (t + 1 < k)
-      cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, plan[t + 1], g.C, wave);
+      copy_k(plan[t + 1]);
     mask_keys(cur);
     softmax_tile_pv<D, SM>(vs, pa, s0, s1, sl2, m, l, oacc, pb, j, half);  // O += P(t-1) V(t-1); P(t)
     wait_tile_copies();  // K(t+1) landed (or the gate rows)
@@ -799,33 +847,12 @@ VsaLayout vsa_layout(int BH, int T, int H, int W, int D) {
   return L;
 }
 
-hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH, int T, int H,
-                             int W, int D, float scale, int topk, double rope_theta,
-                             int rope_precision, int* idx, float* scores_out, void* ws, hipStream_t s) {
-  const Grid3 g = make_grid<Cube>(T, H, W);
-  const VsaLayout L = vsa_layout(BH, T, H, W, D);
-  char* w = static_cast<char*>(ws);
-  auto qc = reinterpret_cast<uint16_t*>(w + L.qc), kc = reinterpret_cast<uint16_t*>(w + L.kc),
-       vct = reinterpret_cast<uint16_t*>(w + L.vct);
-  auto qbar = reinterpret_cast<float*>(w + L.qbar), kbar = reinterpret_cast<float*>(w + L.kbar);
-  auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
-  auto sc = reinterpret_cast<float*>(w + L.scores);
-  auto stat = reinterpret_cast<float2*>(w + L.stat);
-  auto gather = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(256), 0, s, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qc, kc, vct, qbar,
-                       kbar, vbt, g, rope_theta);
-  };
-  hipError_t e;
-  if (rope_theta > 0.0 && rope_precision == 64)
-    e = wf_launch("wf_vsa_gather_rope_fp64", s, [&] { gather(wf_vsa_gather<128, 64>); });
-  else if (rope_theta > 0.0)
-    e = wf_launch("wf_vsa_gather_rope", s, [&] { gather(wf_vsa_gather<128, 32>); });
-  else
-    e = wf_launch("wf_vsa_gather", s, [&] { gather(wf_vsa_gather<128, 0>); });
-  if (e != hipSuccess) return e;
+// Coarse scores and per-row top-k of every head (wf_vsa_scores, then wf_vsa_topk), from the
+// cube means in the workspace.
+static hipError_t launch_scores_topk(const float* qbar, const float* kbar, float* sc, float* scores_out, int* idx,
+                                     float2* stat, int BH, const Grid3& g, float scale, int topk, hipStream_t s) {
   const int ntr = (g.C + 127) / 128, ntc = (g.Cs + 127) / 128;
-  e = wf_launch("wf_vsa_scores", s, [&] {
+  hipError_t e = wf_launch("wf_vsa_scores", s, [&] {
     hipLaunchKernelGGL(wf_vsa_scores<128>, dim3((unsigned)((long)BH * ntr * ntc)), dim3(256), 0, s, qbar,
                        kbar, sc, scores_out, g.C, g.Cs, ntr, ntc, scale);
   });
@@ -851,6 +878,34 @@ hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH
     else if (e <= 48) go(wf_vsa_topk<48>);
     else go(wf_vsa_topk<64>);
   });
+}
+
+hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH, int T, int H,
+                             int W, int D, float scale, int topk, double rope_theta,
+                             int rope_precision, int* idx, float* scores_out, void* ws, hipStream_t s) {
+  const Grid3 g = make_grid<Cube>(T, H, W);
+  const VsaLayout L = vsa_layout(BH, T, H, W, D);
+  char* w = static_cast<char*>(ws);
+  auto qc = reinterpret_cast<uint16_t*>(w + L.qc), kc = reinterpret_cast<uint16_t*>(w + L.kc),
+       vct = reinterpret_cast<uint16_t*>(w + L.vct);
+  auto qbar = reinterpret_cast<float*>(w + L.qbar), kbar = reinterpret_cast<float*>(w + L.kbar);
+  auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
+  auto sc = reinterpret_cast<float*>(w + L.scores);
+  auto stat = reinterpret_cast<float2*>(w + L.stat);
+  auto gather = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(256), 0, s, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qc, kc, vct, qbar,
+                       kbar, vbt, g, rope_theta);
+  };
+  hipError_t e;
+  if (rope_theta > 0.0 && rope_precision == 64)
+    e = wf_launch("wf_vsa_gather_rope_fp64", s, [&] { gather(wf_vsa_gather<128, 64>); });
+  else if (rope_theta > 0.0)
+    e = wf_launch("wf_vsa_gather_rope", s, [&] { gather(wf_vsa_gather<128, 32>); });
+  else
+    e = wf_launch("wf_vsa_gather", s, [&] { gather(wf_vsa_gather<128, 0>); });
+  if (e != hipSuccess) return e;
+  return launch_scores_topk(qbar, kbar, sc, scores_out, idx, stat, BH, g, scale, topk, s);
 }
 
 hipError_t launch_vsa_check(const int* idx, int BH, int C, int topk, void* ws, size_t flag_off,
@@ -886,6 +941,57 @@ hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H,
   if (softmax_mode == kSoftmaxFixedFirst)
     return wf_launch("wf_vsa_fine_fixed_first", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxFixedFirst>); });
   return wf_launch("wf_vsa_fine", s, [&] { go(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded>); });
+}
+
+// The coarse-branch output O_c of every head from the workspace's scores, row statistics and
+// operand-ordered cube means of V.
+static hipError_t launch_coarse_out(const char* w, const VsaLayout& L, const Grid3& g, int BH, float* oc,
+                                    hipStream_t s) {
+  const int rblocks = (g.C + 31) / 32;
+  return wf_launch("wf_vsa_coarse_out", s, [&] {
+    hipLaunchKernelGGL(wf_vsa_coarse_out<128>, dim3((unsigned)(BH * rblocks)), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(w + L.scores),
+                       reinterpret_cast<const float2*>(w + L.stat),
+                       reinterpret_cast<const uint16_t*>(w + L.vbt), oc, g.C, g.Cs, rblocks);
+  });
+}
+
+// VSA in one call: the gather writes only the cube means and V^T (no cube-ordered Q and K), the
+// coarse scores and top-k fill idx, and the fine stage reads Q and K from the token grid; with a
+// gate, the coarse-branch output and the gated merge as in launch_vsa_fine_gated.
+hipError_t launch_vsa_onecall(const void* q, const void* k, const void* v, int BH, int T, int H, int W, int D,
+                              float scale, int topk, int* idx, const void* gate, float* o, float* lse,
+                              float* o_coarse, void* ws, hipStream_t s) {
+  const Grid3 g = make_grid<Cube>(T, H, W);
+  const VsaLayout L = vsa_layout(BH, T, H, W, D);
+  char* w = static_cast<char*>(ws);
+  auto vct = reinterpret_cast<uint16_t*>(w + L.vct);
+  auto qbar = reinterpret_cast<float*>(w + L.qbar), kbar = reinterpret_cast<float*>(w + L.kbar);
+  auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
+  auto qg = static_cast<const uint16_t*>(q), kg = static_cast<const uint16_t*>(k);
+  hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
+    hipLaunchKernelGGL((wf_vsa_gather<128, 0, Cube, true, false>), dim3((unsigned)(BH * g.C)), dim3(256), 0, s,
+                       qg, kg, static_cast<const uint16_t*>(v), nullptr, nullptr, vct, qbar, kbar, vbt, g, 0.0);
+  });
+  if (e != hipSuccess) return e;
+  e = launch_scores_topk(qbar, kbar, reinterpret_cast<float*>(w + L.scores), nullptr, idx,
+                         reinterpret_cast<float2*>(w + L.stat), BH, g, scale, topk, s);
+  if (e != hipSuccess) return e;
+  if (!gate) {
+    return wf_launch("wf_vsa_fine", s, [&] {
+      hipLaunchKernelGGL((wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Cube, true>), dim3((unsigned)(BH * g.C)),
+                         dim3(128), 0, s, qg, kg, vct, idx, o, lse, nullptr, nullptr, g, topk, (long)g.C * topk,
+                         scale * kLog2e);
+    });
+  }
+  float* oc = o_coarse ? o_coarse : reinterpret_cast<float*>(w + L.ocoarse);
+  e = launch_coarse_out(w, L, g, BH, oc, s);
+  if (e != hipSuccess) return e;
+  return wf_launch("wf_vsa_fine_gated", s, [&] {
+    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, true, kSoftmaxGuarded, Cube, true>), dim3((unsigned)(BH * g.C)),
+                       dim3(128), 0, s, qg, kg, vct, idx, o, lse, static_cast<const uint16_t*>(gate), oc, g, topk,
+                       (long)g.C * topk, scale * kLog2e);
+  });
 }
 
 // Sliding-tile attention workspace: the slab-ordered Q, K and V^T, then the slab plan shared by
@@ -940,13 +1046,7 @@ hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   char* w = static_cast<char*>(ws);
   float* oc = o_coarse ? o_coarse : reinterpret_cast<float*>(w + L.ocoarse);
-  const int rblocks = (g.C + 31) / 32;
-  hipError_t e = wf_launch("wf_vsa_coarse_out", s, [&] {
-    hipLaunchKernelGGL(wf_vsa_coarse_out<128>, dim3((unsigned)(BH * rblocks)), dim3(256), 0, s,
-                       reinterpret_cast<const float*>(w + L.scores),
-                       reinterpret_cast<const float2*>(w + L.stat),
-                       reinterpret_cast<const uint16_t*>(w + L.vbt), oc, g.C, g.Cs, rblocks);
-  });
+  hipError_t e = launch_coarse_out(w, L, g, BH, oc, s);
   if (e != hipSuccess) return e;
   return wf_launch("wf_vsa_fine_gated", s, [&] {
     hipLaunchKernelGGL((wf_vsa_fine_fwd<128, true>), dim3((unsigned)(BH * g.C)), dim3(128), 0, s,

@@ -52,6 +52,11 @@ hipError_t launch_vsa_fine(const void* ws, const int* idx, int BH, int T, int H,
 hipError_t launch_vsa_fine_gated(void* ws, const int* idx, const void* gate, int BH, int T, int H,
                                  int W, int D, float scale, int topk, float* o, float* lse,
                                  float* o_coarse, hipStream_t s);
+// VSA in one call (coarse stage and fine stage; no cube-ordered copies of Q and K); with a gate,
+// the coarse-branch output (into o_coarse when not null) and the gated merge.
+hipError_t launch_vsa_onecall(const void* q, const void* k, const void* v, int BH, int T, int H, int W, int D,
+                              float scale, int topk, int* idx, const void* gate, float* o, float* lse,
+                              float* o_coarse, void* ws, hipStream_t s);
 
 // Sliding-tile attention: 6x8x8-token tiles, a (wt, wh, ww)-tile window per query tile; the
 // gather into 1x8x8 slabs, the slab plan (and the tile plan into plan_out, int32
