@@ -434,7 +434,7 @@ def main():
     # extra record (not part of the step): VSA with the gated merge (coarse-branch output plus
     # gate * O_coarse added in the fine stage's epilogue), same inputs and top-k, gate ~ U[0, 1),
     # through the one-call path
-    gated_ms = None
+    gated_ms, plain_fine_ms = None, None
     if not args.no_extra:
         gate = to_dev(synth.make_gate(wv))
 
@@ -452,6 +452,9 @@ def main():
             n, tot = wf.profile_query(name)
             gated_ms[name] = tot / n
         wf.profile_enable(False)
+        # the plain call right after, in the same conditions, for the merge's extra time
+        plain_fine_ms = vsa_kernel_ms(lambda: wf.wf_vsa(qv, kv, vv, grid, wv.topk, idx=idx, out=ov,
+                                                         workspace=ws_v), max(3, args.steps // 2))["wf_vsa_fine"]
         del gate
 
     # extra record (not part of the step): 3D RoPE of Q and K, standalone (wf_rope_qk, the form dense
@@ -708,7 +711,7 @@ def main():
             "kernel_ms": gated_ms,
             "coarse_out_gbs": by_v["coarse_out"] / (gated_ms["wf_vsa_coarse_out"] * 1e-3) / 1e9,
             "coarse_out_frac_hbm": by_v["coarse_out"] / (gated_ms["wf_vsa_coarse_out"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "merge_extra_ms": gated_ms["wf_vsa_fine_gated"] - kern["wf_vsa_fine"],
+            "merge_extra_ms": gated_ms["wf_vsa_fine_gated"] - plain_fine_ms,
             "merge_extra_floor_ms": by_v["merge"] / PEAK_HBM_GBS / 1e6,
         },
         "shape_720p": r720,
