@@ -468,6 +468,8 @@ def main():
             wf.wf_rope_qk(qv, kv, grid, precision=64, q_out=qr, k_out=kr)
             wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v, rope_theta=10000.0)
             wf.wf_vsa_fine(ws_v, idx, (wv.B, wv.Hh, wv.N, wv.D), grid, out=ov)
+            # the same gather without RoPE (it writes the same cube-ordered copies), for the fusion's cost
+            wf.wf_vsa_coarse_topk(qv, kv, vv, grid, wv.topk, idx=idx, workspace=ws_v)
 
         rope_runs()
         torch.cuda.synchronize()
@@ -476,8 +478,8 @@ def main():
             rope_runs()
         torch.cuda.synchronize()
         rk = {}
-        for name in ("wf_rope_qk", "wf_rope_qk_fp64", "wf_vsa_gather_rope", "wf_vsa_scores", "wf_vsa_topk",
-                     "wf_vsa_fine"):
+        for name in ("wf_rope_qk", "wf_rope_qk_fp64", "wf_vsa_gather_rope", "wf_vsa_gather", "wf_vsa_scores",
+                     "wf_vsa_topk", "wf_vsa_fine"):
             n, tot = wf.profile_query(name)
             rk[name] = tot / n
         wf.profile_enable(False)
@@ -490,7 +492,8 @@ def main():
                 "rope_qk_fp64_frac_hbm": rope_bytes / (rk["wf_rope_qk_fp64"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "vsa_ms_per_call_fused_rope": rk["wf_vsa_gather_rope"] + rk["wf_vsa_scores"] + rk["wf_vsa_topk"] + rk["wf_vsa_fine"],
                 "gather_rope_ms": rk["wf_vsa_gather_rope"],
-                "fused_rope_extra_ms": rk["wf_vsa_gather_rope"] - kern["wf_vsa_gather"],
+                "gather_plain_ms": rk["wf_vsa_gather"],
+                "fused_rope_extra_ms": rk["wf_vsa_gather_rope"] - rk["wf_vsa_gather"],
                 "kernel_ms": rk}
         del qr, kr
 
