@@ -134,8 +134,9 @@ size_t wf_vsa_workspace_bytes(int32_t B, int32_t Hh, int32_t T, int32_t H, int32
  *   1. gathers q, k, v into cube order inside `workspace` (padded slots zero);
  *   2. pools cube means Qbar, Kbar, Vbar over each cube's real tokens, in fp32
  *      (Vbar is kept for the coarse-branch output);
- *   3. scores S[c][c'] = scale * Qbar[c] . Kbar[c'] in fp32 and records each
- *      row's softmax maximum and sum;
+ *   3. scores S[c][c'] = scale * Qbar[c] . Kbar[c'] to fp32 accuracy (bf16
+ *      matrix cores on an exact three-part bf16 split of each fp32 mean) and
+ *      records each row's softmax maximum and sum;
  *   4. writes idx[b][h][c][0..topk) = the topk key cubes c' with the largest
  *      S[c][c'], equal scores resolved toward the smaller c', listed in
  *      strictly ascending order.

@@ -412,6 +412,54 @@ def test_near_tie_tolerance_bounds_fp32_scores():
     assert (err <= tau / 4).all()
 
 
+
+def _bf16_rne(x):
+    """fp32 -> nearest bf16 (ties to even), kept as fp32 values (finite inputs)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def test_three_part_bf16_split_scores_within_tau():
+    """Scores from an exact three-part bf16 split of fp32 cube means (hi = bf16(x),
+    mid = bf16(x - hi), lo = bf16(x - hi - mid); hi + mid + lo == x) with the six
+    leading partial products (mid*lo, lo*mid, lo*lo dropped) summed in fp32, in
+    either of two orders, stay within tau/4 of fp64, like plain fp32 dot products."""
+    T, H, W, D = 9, 10, 11, 128
+    N = T * H * W
+    r = rng(15)
+    q, k = (r.normal(size=(N, D)) * 2).astype(np.float32), (r.normal(size=(N, D)) * 2).astype(np.float32)
+    tok = oracle.cube_layout(T, H, W)
+    s = 1 / math.sqrt(D)
+    exact = oracle.coarse_scores(oracle.pool(q.astype(np.float64), tok), oracle.pool(k.astype(np.float64), tok), s)
+    tau = oracle.near_tie_tolerance(q.astype(np.float64), k.astype(np.float64), tok, s)
+    valid = tok >= 0
+
+    def pool32(x):
+        acc = np.zeros((tok.shape[0], D), np.float32)
+        for slot in range(64):
+            acc += np.where(valid[:, slot, None], x[np.maximum(tok[:, slot], 0)], np.float32(0))
+        return acc / valid.sum(axis=1)[:, None].astype(np.float32)
+
+    def split(x):
+        hi = _bf16_rne(x)
+        mid = _bf16_rne(x - hi)
+        lo = _bf16_rne(x - hi - mid)
+        assert np.array_equal(hi.astype(np.float64) + mid + lo, x.astype(np.float64))   # exact
+        return hi, mid, lo
+
+    qp, kp = split(pool32(q)), split(pool32(k))
+    terms = [(2, 0), (1, 1), (0, 2), (1, 0), (0, 1), (0, 0)]       # smallest first
+    for order in (terms, terms[::-1]):
+        s32 = np.zeros((tok.shape[0], tok.shape[0]), np.float32)
+        for d0 in range(0, D, 16):                                   # 16-wide steps, term by term
+            for a, b in order:
+                for d in range(d0, d0 + 16):
+                    s32 += qp[a][:, d:d + 1] * kp[b][None, :, d]   # bf16 x bf16 is exact in fp32
+        s32 *= np.float32(s)
+        err = np.abs(s32.astype(np.float64) - exact).max(axis=1)
+        assert (err <= tau / 4).all()
+
 # --------------------------------------------------------------- coarse branch and gate
 
 def brute_coarse_branch(q, k, v, T, H, W, scale):

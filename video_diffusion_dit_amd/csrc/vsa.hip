@@ -48,6 +48,10 @@ static Grid3 make_grid(int T, int H, int W) {
   return g;
 }
 
+// Blocks of 32 cubes of the stored cube means of Q and K: the scores' 128-wide
+// tiles cover C rounded up to 128 (rows and columns).
+__host__ __device__ constexpr int mean_blocks(int C) { return (C + 127) / 128 * 4; }
+
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -58,6 +62,33 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ long vbar_index(int part, int bh, int BH, int Cs, int key, int d) {
   const int lane = d % 32 + 32 * ((key % 16) / 8);
   return ((((long)part * BH + bh) * (Cs / 16) + key / 16) * 4 + d / 32) * 512 + lane * 8 + key % 8;
+}
+
+// Element offset of (head, cube, head dim, part) in the cube means of Q or K,
+// each fp32 mean stored as three bf16 parts (mean_split), in the operand lane
+// order of the coarse scores' MFMAs (wf_vsa_scores) so that each of a
+// wavefront's operand loads reads 1 KiB contiguously: [bh][block of 32
+// cubes][d step of 16][part hi/mid/lo][lane 0..63][8], lane = cube % 32 +
+// 32 * (d % 16 / 8).  nrb blocks of 32 cubes per head (rows past C are never
+// written; their scores are discarded).
+__device__ __forceinline__ long mean_index(int bh, int nrb, int D, int c, int d, int part) {
+  const int lane = c % 32 + 32 * ((d % 16) / 8);
+  return (((((long)bh * nrb + c / 32) * (D / 16) + d / 16) * 3 + part) * 64 + lane) * 8 + d % 8;
+}
+
+// An fp32 value as three bf16 parts, each rounded to nearest: hi = bf16(x),
+// mid = bf16(x - hi), lo = bf16(x - hi - mid).  Each difference is exact in
+// fp32 and the last one has at most 8 significant bits, so hi + mid + lo == x
+// exactly for every normal x (bf16 keeps fp32's exponent range).
+struct MeanSplit {
+  uint16_t part[3];
+};
+__device__ __forceinline__ MeanSplit mean_split(float x) {
+  const __bf16 h = (__bf16)x;
+  const float r1 = x - (float)h;
+  const __bf16 m = (__bf16)r1;
+  const __bf16 l = (__bf16)(r1 - (float)m);
+  return {{__builtin_bit_cast(uint16_t, h), __builtin_bit_cast(uint16_t, m), __builtin_bit_cast(uint16_t, l)}};
 }
 
 // Token of slot s in block (ct, ch, cw), or -1 for a padded slot.
@@ -77,7 +108,8 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 // ---------------------------------------------------------------- gather + pool
 // One workgroup per (bh, block).  Writes Qc, Kc [BH][C][64][D] (padded slots
 // zero), Vct [BH][C][D][64] (slots in perm16 order) and, with POOL, the fp32
-// means of Q and K over the block's real tokens, and the fp32 mean of V split
+// means of Q and K over the block's real tokens, each as three bf16 parts in
+// the scores' operand order (mean_split, mean_index), and the fp32 mean of V split
 // into two bf16 parts, hi = bf16(mean) and lo = bf16(mean - hi), at key cube c
 // of the operand-ordered means (vbar_index; key cubes C..Cs-1 are zeroed, so
 // the coarse-branch product may run over whole 32-wide steps).  With ROPE, Q
@@ -95,7 +127,7 @@ template <int D, int ROPE, class BLK = Cube, bool POOL = true, bool QK_COPIES = 
 __global__ void __launch_bounds__(256) wf_vsa_gather(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ qc, uint16_t* __restrict__ kc, uint16_t* __restrict__ vct,
-    float* __restrict__ qbar, float* __restrict__ kbar, uint16_t* __restrict__ vbt, Grid3 g,
+    uint16_t* __restrict__ qbar, uint16_t* __restrict__ kbar, uint16_t* __restrict__ vbt, Grid3 g,
     double theta) {
   static_assert(ROPE == 0 || (BLK::BT == 4 && BLK::BH == 4 && BLK::BW == 4), "RoPE is fused for cubes only");
   constexpr int ROWCH = D / 8;            // 16-byte chunks per row
@@ -174,7 +206,10 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
         for (int r = 0; r < RSTEP; ++r) sum += red[r][tid];
         const float mean = sum / (float)count;
         if (which < 2) {
-          (which == 0 ? qbar : kbar)[((long)bh * g.C + c) * D + tid] = mean;
+          const MeanSplit ms = mean_split(mean);
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            (which == 0 ? qbar : kbar)[mean_index(bh, mean_blocks(g.C), D, c, tid, p)] = ms.part[p];
         } else {
           static_assert(D == 128, "four 32-wide head-dim blocks");
           const int BH = gridDim.x / g.C;  // gridDim.x = BH * C
@@ -202,32 +237,41 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
 }
 
 // ---------------------------------------------------------------- coarse scores
-// S[bh][c][c'] = scale * sum_d Qbar[c][d] Kbar[c'][d] in fp32 on the fp32 matrix
-// cores (v_mfma_f32_32x32x2_f32).  One workgroup (4 wavefronts) per 128x128
-// tile of S, a 64x64 tile (2x2 blocks of 32x32) per wavefront, so each operand
-// row a wavefront loads feeds two blocks.  The sum over d is order-free, so
-// lane half h takes d = 32u + 16h + s at step s of chunk u for both operands:
-// each lane's operands are 16 consecutive floats of one row, read straight
-// from memory (L2) as four 16-byte loads, no LDS.  s has row stride Cs and -inf in
-// columns C..Cs-1; s_user (optional) gets the same scores with row stride C.
+// S[bh][c][c'] = scale * sum_d Qbar[c][d] Kbar[c'][d] to fp32 accuracy, from
+// the three-part bf16 split of each fp32 mean (x = hi + mid + lo exactly,
+// mean_split) on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16): the six
+// partial products lo*hi, mid*mid, hi*lo, mid*hi, hi*mid, hi*hi, smallest
+// first, accumulated in fp32.  The three dropped ones (mid*lo, lo*mid, lo*lo)
+// are each below 2^-23 of |Qbar_d Kbar_d|, the order of one fp32 rounding; the
+// six take 6 x 32 matrix-core cycles per 16 d where fp32 MFMAs take 8 x 64.
+// One workgroup (4 wavefronts) per 128x128 tile of S, a 64x64 tile (2x2
+// blocks of 32x32) per wavefront, so each operand row a wavefront loads feeds
+// two blocks.  Lane (j, h) takes d = 16 u + 8 h .. + 7 at step u for both
+// operands, 16 bytes of one part of one row, read straight from memory (L2),
+// no LDS; the means are stored in this lane order (mean_index), so every load
+// of a wavefront reads 1 KiB contiguously (8 cache lines, where row-major
+// means made each load touch 32).  Workgroups are renumbered per XCD
+// (xcd_remap) so each XCD's L2 holds the means of few heads.  s has row stride
+// Cs and -inf in columns C..Cs-1; s_user (optional) gets the same scores with
+// row stride C.
 template <int D>
-__global__ void __launch_bounds__(256) wf_vsa_scores(const float* __restrict__ qbar,
-                                                     const float* __restrict__ kbar,
+__global__ void __launch_bounds__(256) wf_vsa_scores(const uint16_t* __restrict__ qbar,
+                                                     const uint16_t* __restrict__ kbar,
                                                      float* __restrict__ s, float* __restrict__ s_user,
                                                      int C, int Cs, int ntr, int ntc, float scale) {
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, j = lane % 32,
             h = lane / 32;
-  const int per_head = ntr * ntc;
-  const int bh = blockIdx.x / per_head, rem = blockIdx.x % per_head;
+  const int per_head = ntr * ntc, nrb = 4 * ntr;  // ntr = ntc = mean_blocks(C) / 4
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = item / per_head, rem = item % per_head;
   // workgroup tile 128 x 128, wavefront tile 64 x 64 = 2 x 2 blocks of 32 x 32
   const int r0 = (rem / ntc) * 128 + (wave >> 1) * 64, c0 = (rem % ntc) * 128 + (wave & 1) * 64;
-  const float* arow[2];
-  const float* brow[2];
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    arow[x] = qbar + ((long)bh * C + min(r0 + 32 * x + j, C - 1)) * D + h * 16;
-    brow[x] = kbar + ((long)bh * C + min(c0 + 32 * x + j, C - 1)) * D + h * 16;
+    arow[x] = qbar + mean_index(bh, nrb, D, r0 + 32 * x, 0, 0) + lane * 8;
+    brow[x] = kbar + mean_index(bh, nrb, D, c0 + 32 * x, 0, 0) + lane * 8;
   }
   f32x16 acc[2][2];
 #pragma unroll
@@ -236,23 +280,25 @@ __global__ void __launch_bounds__(256) wf_vsa_scores(const float* __restrict__ q
     for (int y = 0; y < 2; ++y)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.f;
-#pragma unroll
-  for (int u = 0; u < D / 32; ++u) {
-    f32x4 a[2][4], bq[2][4];
+  // (A part, B part) of the six products, smallest first: 0 = hi, 1 = mid, 2 = lo
+  constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll 2
+  for (int u = 0; u < D / 16; ++u) {
+    bf16x8 a[2][3], b[2][3];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        a[x][v] = *reinterpret_cast<const f32x4*>(arow[x] + u * 32 + v * 4);
-        bq[x][v] = *reinterpret_cast<const f32x4*>(brow[x] + u * 32 + v * 4);
+      for (int p = 0; p < 3; ++p) {
+        a[x][p] = as_bf16x8(*reinterpret_cast<const uint4*>(arow[x] + (u * 3 + p) * 512));
+        b[x][p] = as_bf16x8(*reinterpret_cast<const uint4*>(brow[x] + (u * 3 + p) * 512));
       }
 #pragma unroll
-    for (int st = 0; st < 16; ++st)
+    for (int t = 0; t < 6; ++t)
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x][st / 4][st % 4], bq[y][st / 4][st % 4], acc[x][y], 0, 0, 0);
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x][PA[t]], b[y][PB[t]], acc[x][y], 0, 0, 0);
   }
   // block (x, y): lane (j, h) holds S[r0 + 32x + 8*(i/4) + 4h + i%4][c0 + 32y + j]
   float* out = s + (long)bh * C * Cs;
@@ -837,8 +883,8 @@ VsaLayout vsa_layout(int BH, int T, int H, int W, int D) {
   L.kc = L.qc + up(tok);
   L.vct = L.kc + up(tok);
   L.qbar = L.vct + up(tok);
-  L.kbar = L.qbar + up((size_t)BH * g.C * D * 4);
-  L.vbt = L.kbar + up((size_t)BH * g.C * D * 4);
+  L.kbar = L.qbar + up((size_t)BH * mean_blocks(g.C) * 32 * D * 3 * 2);
+  L.vbt = L.kbar + up((size_t)BH * mean_blocks(g.C) * 32 * D * 3 * 2);
   L.scores = L.vbt + up((size_t)2 * BH * D * g.Cs * 2);
   L.stat = L.scores + up((size_t)BH * g.C * g.Cs * 4);
   L.ocoarse = L.stat + up((size_t)BH * g.C * 8);
@@ -849,7 +895,7 @@ VsaLayout vsa_layout(int BH, int T, int H, int W, int D) {
 
 // Coarse scores and per-row top-k of every head (wf_vsa_scores, then wf_vsa_topk), from the
 // cube means in the workspace.
-static hipError_t launch_scores_topk(const float* qbar, const float* kbar, float* sc, float* scores_out, int* idx,
+static hipError_t launch_scores_topk(const uint16_t* qbar, const uint16_t* kbar, float* sc, float* scores_out, int* idx,
                                      float2* stat, int BH, const Grid3& g, float scale, int topk, hipStream_t s) {
   const int ntr = (g.C + 127) / 128, ntc = (g.Cs + 127) / 128;
   hipError_t e = wf_launch("wf_vsa_scores", s, [&] {
@@ -888,7 +934,7 @@ hipError_t launch_vsa_coarse(const void* q, const void* k, const void* v, int BH
   char* w = static_cast<char*>(ws);
   auto qc = reinterpret_cast<uint16_t*>(w + L.qc), kc = reinterpret_cast<uint16_t*>(w + L.kc),
        vct = reinterpret_cast<uint16_t*>(w + L.vct);
-  auto qbar = reinterpret_cast<float*>(w + L.qbar), kbar = reinterpret_cast<float*>(w + L.kbar);
+  auto qbar = reinterpret_cast<uint16_t*>(w + L.qbar), kbar = reinterpret_cast<uint16_t*>(w + L.kbar);
   auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
   auto sc = reinterpret_cast<float*>(w + L.scores);
   auto stat = reinterpret_cast<float2*>(w + L.stat);
@@ -966,7 +1012,7 @@ hipError_t launch_vsa_onecall(const void* q, const void* k, const void* v, int B
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   char* w = static_cast<char*>(ws);
   auto vct = reinterpret_cast<uint16_t*>(w + L.vct);
-  auto qbar = reinterpret_cast<float*>(w + L.qbar), kbar = reinterpret_cast<float*>(w + L.kbar);
+  auto qbar = reinterpret_cast<uint16_t*>(w + L.qbar), kbar = reinterpret_cast<uint16_t*>(w + L.kbar);
   auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
   auto qg = static_cast<const uint16_t*>(q), kg = static_cast<const uint16_t*>(k);
   hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
