@@ -6,7 +6,12 @@
 //    descriptor's range check turns into zeros;
 //  * the one-call path's K copy from the token grid (wf_grid.hpp) reads, for every real slot of
 //    every cube of ragged and even grids, exactly the bytes the cube-ordered copy reads for it,
-//    and for a cube index outside [0, C) starts at the head's end.
+//    and for a cube index outside [0, C) starts at the head's end; its V copy reads the same
+//    token rows, chunks placed under the V tile's swizzle (VtrSwz);
+//  * the transpose reads of that V tile (VtrSwz offsets, under the lane mapping of gfx950's
+//    ds_read_b64_tr_b16) deliver to every lane of every P V MFMA exactly the V^T elements its A
+//    operand needs, in the probability registers' key order, and each half wavefront of every
+//    read touches 64 distinct LDS banks.
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -101,17 +106,69 @@ static void grid_copy(int T, int H, int W) {
           const uint64_t off = wf::grid_k_offset(first, i, w, lane, H, W);
           EXPECT(off < (1ull << 31), "grid %dx%dx%d cube %d: offset %llu does not fit\n", T, H, W, cube,
                  (unsigned long long)off);
+          const uint64_t voff = wf::grid_v_offset(first, i, w, lane, H, W, T - 4 * ct, H - 4 * ch, W - 4 * cw,
+                                                   N * 256u);
+          if (!(t < T && h < H && x < W))
+            EXPECT(voff >= (uint64_t)N * 256, "grid %dx%dx%d cube %d: padded V slot %d is read from memory\n", T, H,
+                   W, cube, slot);
           if (t < T && h < H && x < W) {  // a real slot: the bytes the cube-ordered copy reads for it
             const uint64_t tok = ((uint64_t)t * H + h) * W + x;
             const uint64_t want = tok * 256 + (uint64_t)wf::Swz<128>::kslot(slot, lane % 16) * 16;
             EXPECT(off == want, "grid %dx%dx%d cube %d piece %d w %d lane %d: %llu, want %llu\n", T, H, W, cube, i,
                    w, lane, (unsigned long long)off, (unsigned long long)want);
+            const uint64_t vwant = tok * 256 + (uint64_t)wf::VtrSwz::slot(slot, lane % 16) * 16;
+            EXPECT(voff == vwant, "grid %dx%dx%d cube %d V piece %d w %d lane %d\n", T, H, W, cube, i, w, lane);
           }
         }
   }
 }
 
+// The V tile as the copy leaves it in LDS (piece 2i + w, lane l -> LDS bytes 16 (64 (2i + w) + l),
+// the chunk grid_v_offset fetched), then every transpose read of every P V MFMA.
+static void transpose_reads() {
+  int row_of[64 * 16], d0_of[64 * 16];  // per 16-byte LDS chunk: its key row and first dim
+  for (int i = 0; i < 8; ++i)
+    for (int w = 0; w < 2; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        const uint32_t off = wf::grid_v_offset(0, i, w, lane, 4, 4, 4, 4, 4, 64 * 256);  // a 4x4 plane: slot = token
+        const int lds = (64 * (2 * i + w) + lane);                    // 16-byte chunk index in LDS
+        row_of[lds] = (int)(off / 256);
+        d0_of[lds] = (int)(off % 256) / 2;
+      }
+  for (int ks = 0; ks < 4; ++ks)
+    for (int b = 0; b < 4; ++b)
+      for (int r = 0; r < 2; ++r) {
+        int row[64], d0[64];
+        bool bank_used[2][64] = {};
+        for (int L = 0; L < 64; ++L) {
+          const uint32_t a = wf::VtrSwz::offset(wf::VtrSwz::lane_base(L), ks, b, r);
+          EXPECT(a % 8 == 0 && a + 8 <= 64 * 256, "transpose read ks %d b %d r %d lane %d: bad address %u\n", ks, b,
+                 r, L, a);
+          row[L] = row_of[a / 16];
+          d0[L] = d0_of[a / 16] + (int)(a % 16) / 2;
+          for (int x = 0; x < 2; ++x) {
+            const int bank = (int)(a / 4 + x) % 64;
+            EXPECT(!bank_used[L / 32][bank], "transpose read ks %d b %d r %d: bank %d twice in a half wave\n", ks, b,
+                   r, bank);
+            bank_used[L / 32][bank] = true;
+          }
+        }
+        for (int L = 0; L < 64; ++L) {  // lane L = 16 g + i receives element i % 4 of lanes 16 g + 4 e + i / 4
+          const int g = L / 16, i = L % 16, j = L % 32, h = L / 32;
+          for (int e = 0; e < 4; ++e) {
+            const int src = 16 * g + 4 * e + i / 4;
+            const int key = row[src], d = d0[src] + i % 4;
+            const int want_key = 16 * ks + 8 * r + 4 * h + e, want_d = 32 * b + j;  // t = 4 r + e
+            EXPECT(key == want_key && d == want_d,
+                   "transpose read ks %d b %d r %d lane %d element %d: (key %d, d %d), want (%d, %d)\n", ks, b, r, L,
+                   e, key, d, want_key, want_d);
+          }
+        }
+      }
+}
+
 int main() {
+  transpose_reads();
   coverage<128, 2>();
   coverage<128, 4>();
   coverage<64, 4>();

@@ -120,10 +120,14 @@ __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int&
 // precision (32 or 64), 0 for none.  BLK is the block shape (VSA's cubes, or
 // sliding-tile attention's slabs, which need no means).  Q, K, V are read and
 // the copies written with the streaming (non-temporal) policy: each byte is
-// touched once here (3% faster than the default policy at 480p).  Without
-// QK_COPIES only the means of Q and K and the copy of V^T are written (the
-// one-call path's fine stage reads Q and K from the token grid).
-template <int D, int ROPE, class BLK = Cube, bool POOL = true, bool QK_COPIES = true>
+// touched once here (3% faster than the default policy at 480p).  OUT selects
+// what else is written: the cube-ordered Qc and Kc (kOutQK), Vct (kOutVt) and,
+// with POOL, the mean of V (kOutVbar); V is read only for the last two.  The
+// one-call path's fine stage reads Q and K (and, up to some top-k, V) from the
+// token grid, so there the gather writes only the means (and Vct where V is
+// not read from the grid, the mean of V where the coarse branch needs it).
+constexpr int kOutQK = 1, kOutVt = 2, kOutVbar = 4, kOutAll = 7;
+template <int D, int ROPE, class BLK = Cube, bool POOL = true, int OUT = kOutAll>
 __global__ void __launch_bounds__(256) wf_vsa_gather(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ qc, uint16_t* __restrict__ kc, uint16_t* __restrict__ vct,
@@ -137,7 +141,7 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
   constexpr int NTAB = ROPE ? 4 * (sp.t2 + sp.h2 + sp.w2) : 1;
   using CS = RopeCS<ROPE == 64 ? 64 : 32>;
   __shared__ float red[POOL ? RSTEP : 1][D];
-  __shared__ uint16_t vtile[64 * VSTR];
+  __shared__ uint16_t vtile[(OUT & kOutVt) ? 64 * VSTR : 1];
   __shared__ CS tab[NTAB];
   const int tid = threadIdx.x, c16 = tid % ROWCH, r0 = tid / ROWCH;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -161,7 +165,7 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
   const int count = min(BLK::BT, g.T - BLK::BT * ct) * min(BLK::BH, g.H - BLK::BH * ch) *
                     min(BLK::BW, g.W - BLK::BW * cw);
 
-  for (int which = 0; which < 3; ++which) {
+  for (int which = 0; which < ((OUT & (kOutVt | kOutVbar)) ? 3 : 2); ++which) {
     const uint16_t* src = (which == 0 ? q : which == 1 ? k : v) + (long)bh * N * D;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -183,11 +187,11 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       }
       const uint16_t* e = reinterpret_cast<const uint16_t*>(&u);
       if (which < 2) {
-        if constexpr (QK_COPIES) {
+        if constexpr ((OUT & kOutQK) != 0) {
           uint16_t* dst = (which == 0 ? qc : kc) + (cube_row0 + s) * D + c16 * 8;
           __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u), reinterpret_cast<u32x4*>(dst));
         }
-      } else {
+      } else if constexpr ((OUT & kOutVt) != 0) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) vtile[s * VSTR + c16 * 8 + t] = e[t];
       }
@@ -210,7 +214,7 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
 #pragma unroll
           for (int p = 0; p < 3; ++p)
             (which == 0 ? qbar : kbar)[mean_index(bh, mean_blocks(g.C), D, c, tid, p)] = ms.part[p];
-        } else {
+        } else if constexpr ((OUT & kOutVbar) != 0) {
           static_assert(D == 128, "four 32-wide head-dim blocks");
           const int BH = gridDim.x / g.C;  // gridDim.x = BH * C
           const __bf16 h16 = (__bf16)mean;
@@ -222,7 +226,7 @@ __global__ void __launch_bounds__(256) wf_vsa_gather(
       }
     }
     __syncthreads();
-    if (which == 2) {
+    if ((OUT & kOutVt) != 0 && which == 2) {
       uint16_t* dst = vct + ((long)bh * g.C + c) * D * 64;
       for (int id = tid; id < D * 8; id += 256) {
         const int d = id / 8, pc = id % 8;
@@ -576,6 +580,26 @@ __device__ __forceinline__ void grid_k_copy(const uint16_t* khead, uint32_t head
                                              (int)grid_k_offset(first, i, w, lane, g.H, g.W), 0, 0, 0);
 }
 
+// The same for a V tile from the token grid's V, laid out for transpose reads (VtrSwz): the P V
+// operands are then read as V^T without a transposed copy of V.  Slots outside the grid read
+// zeros (grid_v_offset), as in the cube-ordered copy.
+template <int D>
+__device__ __forceinline__ void grid_v_copy(const uint16_t* vhead, uint32_t head_bytes, char* vdst, int cube,
+                                            const Grid3& g, int w, int lane) {
+  static_assert(D == 128, "16 chunks of 16 bytes per row");
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const uint32_t first = cube_first_token(cube, g.C, g.nh, g.nw, g.H, g.W, head_bytes / (D * 2));
+  int kt, kh, kw;
+  cube_coords(g, cube, kt, kh, kw);
+  const int lt = g.T - 4 * kt, lh = g.H - 4 * kh, lw = g.W - 4 * kw;
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vhead, head_bytes);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (lds_ptr)(vdst + (i * 2 + w) * 1024), 16,
+        (int)grid_v_offset(first, i, w, lane, g.H, g.W, lt, lh, lw, head_bytes), 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- fine stage
 // P V of the previous tile interleaved with the probabilities of the current
 // one (p = 2^(s*sl2 - m) in bf16, as tile_probs): step i computes probability
@@ -589,13 +613,13 @@ __device__ __forceinline__ void grid_k_copy(const uint16_t* khead, uint32_t head
 // ends by reading the last MFMA's result, which waits for the matrix pipe to
 // drain before any later instruction may reuse those registers.  Returns the
 // lane's sum of the new probabilities, summed in tile_probs' order.
-template <int D>
+template <int D, bool VTR = false>
 __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_old, f32x16* o, const f32x16& s0,
                                                const f32x16& s1, float sl2, float m, bf16x2* p_new, int j,
                                                int half) {
   constexpr int NPV = Pairs<D>::NPV, PF = kRingPF, R = kRing;
   static_assert(NPV == 16 && D == 128, "one probability pair per P V MFMA");
-  OperandBase<D> ob(j, half);
+  OperandBase<D, VTR> ob(j, half);
   asm volatile("" : "+v"(ob.k), "+v"(ob.v));
   bf16x8 pg[4];  // B operand of the k-step ks: probabilities 4 ks .. 4 ks + 3
 #pragma unroll
@@ -603,14 +627,14 @@ __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_o
     pg[g] = __builtin_bit_cast(bf16x8, P4{p_old[4 * g], p_old[4 * g + 1], p_old[4 * g + 2], p_old[4 * g + 3]});
   uint4 ring[R];
 #pragma unroll
-  for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D>(u, vt, nullptr, ob);
+  for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D, VTR>(u, vt, nullptr, ob);
   const float nm = -m;
   const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
   float la = 0.f, lb = 0.f;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
-    if (i + PF < NPV) ring[(i + PF) % R] = mfma_operand<D>(i + PF, vt, nullptr, ob);
+    if (i + PF < NPV) ring[(i + PF) % R] = mfma_operand<D, VTR>(i + PF, vt, nullptr, ob);
     __builtin_amdgcn_sched_barrier(0);
     const f32x16& sv = i < 8 ? s0 : s1;
     const int r = i % 8;
@@ -638,21 +662,21 @@ __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_o
 // softmax_tile for tile t with P(t-1) V(t-1) run inside it (pv_with_probs).
 // The arithmetic is softmax_tile's, in the same order relative to O: P V of
 // tile t-1 is accumulated before O is rescaled for tile t's reference.
-template <int D, int SM>
+template <int D, int SM, bool VTR = false>
 __device__ __forceinline__ void softmax_tile_pv(const char* vt, const bf16x2* p_old, const f32x16& s0,
                                                 const f32x16& s1, float sl2, float& m, float& l, f32x16* o,
                                                 bf16x2* p_new, int j, int half) {
   constexpr int DB = D / 32;
   if constexpr (SM == kSoftmaxRunningMax) {
     const float mnew = fmaxf(m, tile_row_max(s0, s1, sl2));
-    const float lt = pv_with_probs<D>(vt, p_old, o, s0, s1, sl2, mnew, p_new, j, half);
+    const float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, mnew, p_new, j, half);
     rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
     m = mnew;
     l += lt;
   } else if constexpr (SM == kSoftmaxFixedFirst) {
-    l += pv_with_probs<D>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
+    l += pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
   } else {
-    float lt = pv_with_probs<D>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
+    float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
     if (__ballot(!(lt <= 0x1p16f))) {  // a big jump (the first tile is not run here)
       const float mnew = fmaxf(m, ceilf(tile_row_max(s0, s1, sl2)));
       rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
@@ -678,12 +702,14 @@ __device__ __forceinline__ void softmax_tile_pv(const char* vt, const bf16x2* p_
 // query cube (gated merge); the last tile loads the gate rows where other
 // tiles copy the next K cube.  SM selects the softmax reference policy
 // (softmax_tile).  BLK is the shape of the 64-token blocks (VSA's cubes;
-// sliding-tile attention's slabs).  With GRID_QK, qc and kc are the token-grid
-// Q and K themselves ([BH][N][D]): the query rows are loaded by token (padded
-// slots get zero rows, as in the cube-ordered copy, so the result is the same
-// bit for bit) and the K tiles are copied with grid_k_copy, so the gather need
-// not write cube-ordered copies of them.
-template <int D, bool GATED, int SM = kSoftmaxGuarded, class BLK = Cube, bool GRID_QK = false>
+// sliding-tile attention's slabs).  With GRID_QK, qc and kc are the
+// token-grid Q and K themselves ([BH][N][D]): the query rows are loaded by
+// token (padded slots get zero rows, as in the cube-ordered copy) and the K
+// tiles are copied with grid_k_copy.  With GRID_V, vct is the token-grid V
+// too: its tiles are copied with grid_v_copy and the P V operands read from
+// them with transpose reads (VtrSwz), so the gather need not write the
+// transposed copy Vct.  The output is the same bit for bit either way.
+template <int D, bool GATED, int SM = kSoftmaxGuarded, class BLK = Cube, bool GRID_QK = false, bool GRID_V = false>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vct, const int* __restrict__ idx, float* __restrict__ o,
@@ -734,7 +760,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   // the head's cube-ordered K and V^T: every copy is range-checked against these C cubes, so a
   // plan entry outside [0, C) reads zeros (cube_copy) instead of memory beyond them
   const uint16_t* khead = GRID_QK ? kc + head_row0 * D : kc + cube_base * 64 * D;
-  const uint16_t* vhead = vct + cube_base * D * 64;
+  const uint16_t* vhead = GRID_V ? vct + head_row0 * D : vct + cube_base * D * 64;
   // the next K tile: from the cube-ordered copy, or (GRID_QK) from the token grid
   auto copy_k = [&](int cube) __attribute__((always_inline)) {
     if constexpr (GRID_QK)
@@ -742,9 +768,16 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     else
       cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, cube, g.C, wave);
   };
+  // the V tile of a cube: V^T from the cube-ordered copy, or (GRID_V) V from the token grid
+  auto copy_v = [&](int cube) __attribute__((always_inline)) {
+    if constexpr (GRID_V)
+      grid_v_copy<D>(vhead, (uint32_t)(N * D * 2), vs, cube, g, wave, lane);
+    else
+      cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cube, g.C, wave);
+  };
   int cur = plan[0];
   copy_k(cur);
-  cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cur, g.C, wave);
+  copy_v(cur);
   wait_tile_copies_keep<VP>();  // K(0) landed; V(0) may still fly
   GatePre gp;
   // masks the padded key slots of an edge block.  Each score is rewritten through a select that
@@ -789,10 +822,10 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     else if (t + 1 < k)
       copy_k(plan[t + 1]);
     mask_keys(cur);
-    softmax_tile_pv<D, SM>(vs, pa, s0, s1, sl2, m, l, oacc, pb, j, half);  // O += P(t-1) V(t-1); P(t)
+    softmax_tile_pv<D, SM, GRID_V>(vs, pa, s0, s1, sl2, m, l, oacc, pb, j, half);  // O += P(t-1) V(t-1); P(t)
     wait_tile_copies();  // K(t+1) landed (or the gate rows)
     barrier_nofence();   // V slot free; K(t+1) visible
-    cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cur, g.C, wave);  // V(t)
+    copy_v(cur);  // V(t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) pa[i] = pb[i];
   };
@@ -807,7 +840,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   if constexpr (GATED) {  // a single tile had no later tile to load them in
     if (k == 1) gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
   }
-  mfma_run<D, 0, NPV>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // O += P(k-1) V(k-1)
+  mfma_run<D, 0, NPV, GRID_V>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // O += P(k-1) V(k-1)
   wait_tile_copies();  // the gate rows (k = 1)
   barrier_nofence();   // every wavefront is done with both slots
   const float lt = l + __shfl_xor(l, 32);
@@ -1005,6 +1038,12 @@ static hipError_t launch_coarse_out(const char* w, const VsaLayout& L, const Gri
 // VSA in one call: the gather writes only the cube means and V^T (no cube-ordered Q and K), the
 // coarse scores and top-k fill idx, and the fine stage reads Q and K from the token grid; with a
 // gate, the coarse-branch output and the gated merge as in launch_vsa_fine_gated.
+// The one-call path reads V from the token grid (no transposed copy in the gather, transpose
+// reads in the fine stage) up to this top-k: the copy it saves is a fixed cost per call, the
+// transpose reads and strided V tiles an extra cost per tile (at 480p the call is 3% faster at
+// top-32 and 1% slower at top-78 this way).
+constexpr int kGridVMaxTopk = 48;
+
 hipError_t launch_vsa_onecall(const void* q, const void* k, const void* v, int BH, int T, int H, int W, int D,
                               float scale, int topk, int* idx, const void* gate, float* o, float* lse,
                               float* o_coarse, void* ws, hipStream_t s) {
@@ -1014,29 +1053,46 @@ hipError_t launch_vsa_onecall(const void* q, const void* k, const void* v, int B
   auto vct = reinterpret_cast<uint16_t*>(w + L.vct);
   auto qbar = reinterpret_cast<uint16_t*>(w + L.qbar), kbar = reinterpret_cast<uint16_t*>(w + L.kbar);
   auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
-  auto qg = static_cast<const uint16_t*>(q), kg = static_cast<const uint16_t*>(k);
+  auto qg = static_cast<const uint16_t*>(q), kg = static_cast<const uint16_t*>(k),
+       vg = static_cast<const uint16_t*>(v);
+  const bool grid_v = topk <= kGridVMaxTopk;
+  // the means, the mean of V for the coarse branch when there is a gate, Vct unless V is read from
+  // the grid
+  auto gather = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(256), 0, s, qg, kg, vg, nullptr, nullptr, vct,
+                       qbar, kbar, vbt, g, 0.0);
+  };
   hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
-    hipLaunchKernelGGL((wf_vsa_gather<128, 0, Cube, true, false>), dim3((unsigned)(BH * g.C)), dim3(256), 0, s,
-                       qg, kg, static_cast<const uint16_t*>(v), nullptr, nullptr, vct, qbar, kbar, vbt, g, 0.0);
+    if (grid_v) {
+      if (gate) gather(wf_vsa_gather<128, 0, Cube, true, kOutVbar>);
+      else gather(wf_vsa_gather<128, 0, Cube, true, 0>);
+    } else {
+      if (gate) gather(wf_vsa_gather<128, 0, Cube, true, kOutVt | kOutVbar>);
+      else gather(wf_vsa_gather<128, 0, Cube, true, kOutVt>);
+    }
   });
   if (e != hipSuccess) return e;
   e = launch_scores_topk(qbar, kbar, reinterpret_cast<float*>(w + L.scores), nullptr, idx,
                          reinterpret_cast<float2*>(w + L.stat), BH, g, scale, topk, s);
   if (e != hipSuccess) return e;
+  const uint16_t* vsrc = grid_v ? vg : vct;
+  auto fine = [&](auto kernel, const uint16_t* gt, const float* oc) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(128), 0, s, qg, kg, vsrc, idx, o, lse, gt, oc, g,
+                       topk, (long)g.C * topk, scale * kLog2e);
+  };
   if (!gate) {
     return wf_launch("wf_vsa_fine", s, [&] {
-      hipLaunchKernelGGL((wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Cube, true>), dim3((unsigned)(BH * g.C)),
-                         dim3(128), 0, s, qg, kg, vct, idx, o, lse, nullptr, nullptr, g, topk, (long)g.C * topk,
-                         scale * kLog2e);
+      if (grid_v) fine(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Cube, true, true>, nullptr, nullptr);
+      else fine(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Cube, true, false>, nullptr, nullptr);
     });
   }
   float* oc = o_coarse ? o_coarse : reinterpret_cast<float*>(w + L.ocoarse);
   e = launch_coarse_out(w, L, g, BH, oc, s);
   if (e != hipSuccess) return e;
+  auto gt = static_cast<const uint16_t*>(gate);
   return wf_launch("wf_vsa_fine_gated", s, [&] {
-    hipLaunchKernelGGL((wf_vsa_fine_fwd<128, true, kSoftmaxGuarded, Cube, true>), dim3((unsigned)(BH * g.C)),
-                       dim3(128), 0, s, qg, kg, vct, idx, o, lse, static_cast<const uint16_t*>(gate), oc, g, topk,
-                       (long)g.C * topk, scale * kLog2e);
+    if (grid_v) fine(wf_vsa_fine_fwd<128, true, kSoftmaxGuarded, Cube, true, true>, gt, oc);
+    else fine(wf_vsa_fine_fwd<128, true, kSoftmaxGuarded, Cube, true, false>, gt, oc);
   });
 }
 

@@ -184,21 +184,37 @@ struct Pairs {
 // and the 32-row block).  The bases are made opaque once per run so the
 // compiler computes the XORs in place instead of keeping one register per
 // k-step alive across the loop.
-template <int D>
+// With VTR the V operand comes from a V tile ([keys][D], VtrSwz) through two
+// transpose reads instead of one read of a V^T tile.
+template <int D, bool VTR = false>
 struct OperandBase {
   uint32_t k, v;
   __device__ __forceinline__ OperandBase(int j, int half) {
     const int kf = Swz<D>::KCPR == 16 ? (j & 15) : ((j >> 1) & 7);
     k = (uint32_t)(j * D * 2 + 16 * (half ^ kf));
-    v = (uint32_t)(j * 128 + 16 * (half ^ ((j >> 1) & 7)));
+    v = VTR ? VtrSwz::lane_base(j + 32 * half) : (uint32_t)(j * 128 + 16 * (half ^ ((j >> 1) & 7)));
   }
 };
 
+// V operand of P V pair (ks, b) from a V tile: transpose reads r = 0 and 1 give elements 0..3 and
+// 4..7 (keys 16 ks + 8 r + 4 half + 0..3 of dim 32 b + j).
 template <int D>
-__device__ __forceinline__ uint4 mfma_operand(int i, const char* vt, const char* kt, const OperandBase<D>& ob) {
+__device__ __forceinline__ uint4 vtr_operand(const char* v, uint32_t base, int ks, int b) {
+  static_assert(D == 128, "V tile rows of 256 bytes");
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef short s8 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) s4* lds_s4;
+  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(v + VtrSwz::offset(base, ks, b, 0)));
+  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(v + VtrSwz::offset(base, ks, b, 1)));
+  return __builtin_bit_cast(uint4, (s8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D, bool VTR = false>
+__device__ __forceinline__ uint4 mfma_operand(int i, const char* vt, const char* kt, const OperandBase<D, VTR>& ob) {
   constexpr int NPV = Pairs<D>::NPV;
   if (i < NPV) {  // ks = i / (D/32), block b = i % (D/32): V^T rows b*32 + j
     const int ks = i / (D / 32), b = i % (D / 32);
+    if constexpr (VTR) return vtr_operand<D>(vt, ob.v, ks, b);
     return *reinterpret_cast<const uint4*>(vt + b * 32 * 128 + (ob.v ^ (uint32_t)(32 * ks)));
   }
   const int kk = (i - NPV) / 2, kb = (i - NPV) % 2;  // K rows kb*32 + j
@@ -230,15 +246,15 @@ __device__ __forceinline__ void mfma_pair(int i, uint4 a, const bf16x2* p2, cons
 // so the run starts its first MFMA without waiting for LDS).
 constexpr int kRingPF = 4, kRing = kRingPF + 1;
 
-template <int D, int I0>
+template <int D, int I0, bool VTR = false>
 __device__ __forceinline__ void mfma_prefill(uint4 (&ring)[kRing], const char* vt, const char* kt, int j, int half) {
-  OperandBase<D> ob(j, half);
+  OperandBase<D, VTR> ob(j, half);
   asm volatile("" : "+v"(ob.k), "+v"(ob.v));
 #pragma unroll
-  for (int u = 0; u < kRingPF; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, ob);
+  for (int u = 0; u < kRingPF; ++u) ring[u] = mfma_operand<D, VTR>(I0 + u, vt, kt, ob);
 }
 
-template <int D, int I0, int I1, bool PREFILLED = false>
+template <int D, int I0, int I1, bool PREFILLED = false, bool VTR = false>
 __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
                                          f32x16* o, f32x16& s0, f32x16& s1, int j, int half,
                                          uint4 (&ring)[kRing]) {
@@ -248,26 +264,26 @@ __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const b
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
   }
-  OperandBase<D> ob(j, half);
+  OperandBase<D, VTR> ob(j, half);
   asm volatile("" : "+v"(ob.k), "+v"(ob.v));
   if constexpr (!PREFILLED) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D>(I0 + u, vt, kt, ob);
+    for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D, VTR>(I0 + u, vt, kt, ob);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    if (i + PF < NP) ring[(i + PF) % R] = mfma_operand<D>(I0 + i + PF, vt, kt, ob);
+    if (i + PF < NP) ring[(i + PF) % R] = mfma_operand<D, VTR>(I0 + i + PF, vt, kt, ob);
     mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int D, int I0, int I1>
+template <int D, int I0, int I1, bool VTR = false>
 __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
                                          f32x16* o, f32x16& s0, f32x16& s1, int j, int half) {
   uint4 ring[kRing];
-  mfma_run<D, I0, I1, false>(vt, kt, p2, qop, o, s0, s1, j, half, ring);
+  mfma_run<D, I0, I1, false, VTR>(vt, kt, p2, qop, o, s0, s1, j, half, ring);
 }
 
 // ------------------------------------------------------------- softmax tile

@@ -1,5 +1,5 @@
-// Offsets of the key-tile copy that reads one 4x4x4 key cube of K straight from the token grid
-// (the one-call VSA path, which skips the cube-ordered copy of K).  Plain C++ for host and
+// Offsets of the key-tile copies that read one 4x4x4 key cube of K and V straight from the token
+// grid (the one-call VSA path, which skips the cube-ordered copies of K and V).  Plain C++ for host and
 // device, so the arithmetic can be checked on the host.
 #pragma once
 
@@ -26,6 +26,19 @@ WF_HD constexpr uint32_t grid_k_offset(uint32_t first_token, int i, int w, int l
   const int sr = 2 * i + w, dw = lane / 16;
   const uint32_t tok = first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W + dw);
   return tok * 256u + (uint32_t)Swz<128>::kslot(4 * sr + dw, lane % 16) * 16u;
+}
+
+// The same for a V tile read by transpose reads (VtrSwz): the same pieces and slots, the
+// chunk placed under the V tile's swizzle.  A slot outside the grid (the cube's first lt, lh, lw
+// slot coordinates along t, h, w are inside it) gets head_bytes, which the range check turns
+// into zeros, as the cube-ordered copy holds there: its probability is zero, and a zero row
+// keeps it so whatever the other rows of V hold.
+WF_HD constexpr uint32_t grid_v_offset(uint32_t first_token, int i, int w, int lane, int H, int W, int lt, int lh,
+                                       int lw, uint32_t head_bytes) {
+  const int sr = 2 * i + w, dw = lane / 16;
+  const uint32_t tok = first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W + dw);
+  return (sr / 4 < lt && sr % 4 < lh && dw < lw) ? tok * 256u + (uint32_t)VtrSwz::slot(4 * sr + dw, lane % 16) * 16u
+                                                   : head_bytes;
 }
 
 }  // namespace wf

@@ -34,6 +34,35 @@ struct Swz {
   WF_HD static constexpr int vslot(int d, int c) { return c ^ ((d >> 1) & 7); }
 };
 
+// A V tile stored like a K tile, [64 keys][128] bf16 (no transpose), for P V
+// operands read with the gfx950 LDS transpose read ds_read_b64_tr_b16.  That
+// instruction works on each group of 16 lanes: lane s of the group supplies
+// the address of 4 consecutive bf16 (8 bytes), and lane i of the group
+// receives element i % 4 of the chunks of lanes i / 4, 4 + i / 4, 8 + i / 4
+// and 12 + i / 4, in that order (measured on gfx950).  The P V MFMA's A
+// operand for key step ks (16 keys) and head-dim block b (32 dims) is
+// V^T[32 b + j][keys of the probability layout], lane (j, h) element t being
+// key 16 ks + 8 (t / 4) + 4 h + t % 4 -- the order in which the score
+// registers hold P, so no key permutation is stored.  Two transpose reads
+// (r = t / 4) give the 8 elements: lane L = 16 g + 4 e + q (g = group, e, q
+// in 0..3) reads row 16 ks + 8 r + 4 (g / 2) + e at dims 32 b + 16 (g % 2) +
+// 4 q .. + 3.  The 16-byte chunk c of row r sits at chunk slot
+// c ^ (4 (r % 4) + (r / 4) % 4) of the row, which puts the 32 lanes of each
+// half wavefront on 64 distinct LDS banks.
+struct VtrSwz {
+  WF_HD static constexpr int slot(int r, int c) { return c ^ (4 * (r & 3) + ((r >> 2) & 3)); }
+  // lane-dependent part of the transpose-read byte offset: row 4 (g / 2) + e, slot bits
+  // 4 e + ((2 (g % 2) + q / 2) ^ (g / 2)), half q % 2 of the chunk
+  WF_HD static constexpr uint32_t lane_base(int lane) {
+    const int g = (lane >> 4) & 3, e = (lane >> 2) & 3, q = lane & 3;
+    return (uint32_t)((4 * (g >> 1) + e) * 256 + (4 * e + ((2 * (g & 1) + (q >> 1)) ^ (g >> 1))) * 16 + (q & 1) * 8);
+  }
+  // byte offset in the tile of transpose read r of key step ks and dim block b
+  WF_HD static constexpr uint32_t offset(uint32_t base, int ks, int b, int r) {
+    return (base ^ (uint32_t)((4 * b + 2 * r) * 16)) + (uint32_t)((16 * ks + 8 * r) * 256);
+  }
+};
+
 // Global -> LDS tile copies by NWC wavefronts.  Wavefront w copies K pieces
 // g = i * NWC + w (i < KPW), each 1 KiB of the K tile's LDS image: lane L
 // fetches the 16-byte chunk that belongs at LDS byte g * 1024 + 16 L under the
