@@ -1,7 +1,9 @@
 """The kernels' copy offsets evaluated on the host (no GPU): full coverage of every tile
 copy, fine-stage reads confined to the selected cube or, for a plan entry outside [0, C),
-past the end of the head's region, where the buffer range check returns zeros, and the
-one-call path's K copy from the token grid reading exactly what the cube-ordered copy reads."""
+past the end of the head's region, where the buffer range check returns zeros, the
+one-call path's K and V copies from the token grid reading exactly what the cube-ordered copy
+reads (padded V slots reading zeros), and its LDS transpose reads handing every P V MFMA lane
+the V^T elements it needs, on 64 distinct banks per half wavefront."""
 import os
 import shutil
 import subprocess
