@@ -131,9 +131,6 @@ def ideal_speedup(wl, C) -> float:
     return dense_flops(wl) / vsa_flops(wl, C)["total"]
 
 
-GRID_V_MAX_TOPK = 48   # the one-call path reads V from the token grid up to this top-k
-
-
 def vsa_bytes(wl, C, gated=False) -> dict:
     """Algorithmic HBM bytes per call of each VSA kernel (Cs: C rounded up to 32).  The cube means
     of Q and K are stored as three bf16 parts (6 bytes per element), V's as two."""
@@ -141,12 +138,9 @@ def vsa_bytes(wl, C, gated=False) -> dict:
     BH = wl.B * wl.Hh
     means_qk, means_v = 2 * C * wl.D * 6, 2 * wl.D * Cs * 2
     gather = BH * (3 * wl.N * wl.D * 2 + 3 * Np * wl.D * 2 + means_qk + means_v)
-    # the one-call path's gather writes no cube-ordered Q and K; up to GRID_V_MAX_TOPK no V^T
-    # either, and it reads V only for V's mean, which only the gated coarse branch needs
-    grid_v = wl.topk <= GRID_V_MAX_TOPK
-    reads_v = gated or not grid_v
-    gather_one_call = BH * ((3 if reads_v else 2) * wl.N * wl.D * 2 + (0 if grid_v else Np * wl.D * 2) + means_qk
-                            + (means_v if gated else 0))
+    # the one-call path's gather writes no cube-ordered Q, K or V, and reads V only for V's mean,
+    # which only the gated coarse branch needs
+    gather_one_call = BH * ((3 if gated else 2) * wl.N * wl.D * 2 + means_qk + (means_v if gated else 0))
     scores = BH * (2 * C * wl.D * 6 + C * Cs * 4)
     topk = BH * (C * C * 4 + C * wl.topk * 4 + C * 8)
     # coarse-branch output: scores + row statistics + hi/lo cube means of V in, O_coarse out

@@ -186,10 +186,9 @@ int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t
  * VSA in one call: the coarse stage and the fine stage of wf_vsa_coarse_topk
  * followed by wf_vsa_fine (or, with a gate, wf_vsa_fine_gated) on the plan it
  * selects, with the same result (o, lse, idx and o_coarse bit for bit).  The
- * one call needs no cube-ordered copies of Q and K: the fine stage reads them
- * from q and k in grid order, and up to topk = 48 it reads v there too (with
- * LDS transpose reads), so the gather writes no transposed copy of V either
- * and moves about a third (up to top-48: over half) fewer bytes.
+ * one call needs no cube-ordered copies of Q, K and V: the fine stage reads
+ * q, k and v in grid order (v with LDS transpose reads), so the gather only
+ * pools the cube means and moves under a third of the bytes.
  *
  *   q, k, v        bf16 [B][Hh][T*H*W][D], read only; D must be 128.
  *   topk           1 <= topk <= C.
@@ -201,7 +200,7 @@ int32_t wf_vsa_fine(const void* workspace, size_t workspace_bytes, const int32_t
  *                  NULL without a gate.
  *   workspace      at least wf_vsa_workspace_bytes(); its contents afterwards
  *                  are not a workspace that wf_vsa_fine or wf_vsa_fine_gated
- *                  can take (the cube-ordered Q, K and V are not all written).
+ *                  can take (the cube-ordered Q, K and V are not written).
  */
 int32_t wf_vsa(const void* q, const void* k, const void* v, int32_t B, int32_t Hh, int32_t T, int32_t H,
                int32_t W, int32_t D, float scale, int32_t topk, int32_t* idx, const void* gate, float* o,

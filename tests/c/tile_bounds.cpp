@@ -8,6 +8,7 @@
 //    every cube of ragged and even grids, exactly the bytes the cube-ordered copy reads for it,
 //    and for a cube index outside [0, C) starts at the head's end; its V copy reads the same
 //    token rows, chunks placed under the V tile's swizzle (VtrSwz);
+//  * block coordinates by multiply-high division (div_magic) match plain division;
 //  * the transpose reads of that V tile (VtrSwz offsets, under the lane mapping of gfx950's
 //    ds_read_b64_tr_b16) deliver to every lane of every P V MFMA exactly the V^T elements its A
 //    operand needs, in the probability registers' key order, and each half wavefront of every
@@ -167,7 +168,36 @@ static void transpose_reads() {
       }
 }
 
+// The block-coordinate division by multiply-high (div_magic) is exact for every block index
+// below 4096 and divisor up to 4096 (and a sample of larger divisors), and block coordinates
+// computed with it give cube_first_token's first tokens.
+static void magic_division() {
+  for (uint32_t d = 1; d <= 4096; ++d) {
+    const uint32_t m = wf::div_magic(d);
+    for (uint32_t n = 0; n < 4096; ++n)
+      EXPECT(wf::div_by_magic(n, m) == n / d, "div_by_magic(%u, magic(%u)) = %u, want %u\n", n, d,
+             wf::div_by_magic(n, m), n / d);
+  }
+  for (uint32_t d = 4097; d < (1u << 20); d += 997) {
+    const uint32_t m = wf::div_magic(d);
+    for (uint32_t n = 0; n < 4096; n += 7) EXPECT(wf::div_by_magic(n, m) == n / d, "large divisor %u\n", d);
+  }
+  const int grids[][3] = {{1, 1, 1}, {5, 6, 7}, {21, 30, 52}, {21, 45, 80}, {13, 6, 21}, {64, 64, 64}};
+  for (const auto& gr : grids) {
+    const int T = gr[0], H = gr[1], W = gr[2];
+    const int nh = (H + 3) / 4, nw = (W + 3) / 4, C = (T + 3) / 4 * nh * nw;
+    const uint32_t mhw = wf::div_magic((uint32_t)(nh * nw)), mw = wf::div_magic((uint32_t)nw);
+    for (int c = 0; c < C; ++c) {
+      const int ct = (int)wf::div_by_magic((uint32_t)c, mhw), r = c - ct * nh * nw;
+      const int ch = (int)wf::div_by_magic((uint32_t)r, mw), cw = r - ch * nw;
+      EXPECT(wf::cube_first_token_at(ct, ch, cw, H, W) == wf::cube_first_token(c, C, nh, nw, H, W, T * H * W),
+             "grid %dx%dx%d cube %d: first token differs\n", T, H, W, c);
+    }
+  }
+}
+
 int main() {
+  magic_division();
   transpose_reads();
   coverage<128, 2>();
   coverage<128, 4>();

@@ -234,10 +234,9 @@ def test_vsa_fine_edge_cube_plans(wf, plan):
                                             ((13, 6, 21), 17, 1, 2), ((21, 30, 52), 32, 1, 3),
                                             ((9, 17, 29), 64, 1, 2), ((21, 30, 52), 78, 1, 1)])
 def test_vsa_one_call_equals_two_calls(wf, grid, topk, B, Hh):
-    """wf_vsa (no cube-ordered copies of Q and K; the fine stage reads them from the token grid,
-    and V too up to top-48, through transpose reads, beyond it from the transposed copy) gives the
-    plan, O and lse of wf_vsa_coarse_topk + wf_vsa_fine bit for bit, and O matches the oracle's
-    fine stage on that plan."""
+    """wf_vsa (no cube-ordered copies of Q, K and V; the fine stage reads them from the token grid,
+    V through transpose reads) gives the plan, O and lse of wf_vsa_coarse_topk + wf_vsa_fine bit for
+    bit, and O matches the oracle's fine stage on that plan, up to top-78."""
     import torch
     T, H, W = grid
     wl = synth.small_workload("vsa_one_call", B, Hh, T, H, W, 128, structured=True, seed=T * 7 + topk, topk=topk)

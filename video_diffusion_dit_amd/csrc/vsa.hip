@@ -36,15 +36,19 @@ using Slab = Block<1, 8, 8>;
 // The block grid of a T x H x W token grid (each axis padded up to a whole
 // number of blocks).  Cs: the block count rounded up to a multiple of 32, the
 // row stride of the coarse scores and of the transposed cube means of V.
+// mnw, mnhw: div_magic of nw and nh * nw, so that block coordinates cost two multiply-highs.
 struct Grid3 {
   int T, H, W, nt, nh, nw, C, Cs;
+  uint32_t mnw, mnhw;
 };
 
 template <class BLK>
 static Grid3 make_grid(int T, int H, int W) {
-  Grid3 g{T, H, W, (T + BLK::BT - 1) / BLK::BT, (H + BLK::BH - 1) / BLK::BH, (W + BLK::BW - 1) / BLK::BW, 0, 0};
+  Grid3 g{T, H, W, (T + BLK::BT - 1) / BLK::BT, (H + BLK::BH - 1) / BLK::BH, (W + BLK::BW - 1) / BLK::BW, 0, 0, 0, 0};
   g.C = g.nt * g.nh * g.nw;
   g.Cs = (g.C + 31) / 32 * 32;
+  g.mnw = div_magic((uint32_t)g.nw);
+  g.mnhw = div_magic((uint32_t)(g.nh * g.nw));
   return g;
 }
 
@@ -99,10 +103,32 @@ __device__ __forceinline__ int slot_token(const Grid3& g, int ct, int ch, int cw
   return (t < g.T && h < g.H && w < g.W) ? (t * g.H + h) * g.W + w : -1;
 }
 
+// Block coordinates of block c (0 <= c < C <= 4096; any other c gives some coordinates, which
+// callers do not use to address memory).
 __device__ __forceinline__ void cube_coords(const Grid3& g, int c, int& ct, int& ch, int& cw) {
-  cw = c % g.nw;
-  ch = (c / g.nw) % g.nh;
-  ct = c / (g.nw * g.nh);
+  ct = (int)div_by_magic((uint32_t)c, g.mnhw);
+  const int r = c - ct * g.nh * g.nw;
+  ch = (int)div_by_magic((uint32_t)r, g.mnw);
+  cw = r - ch * g.nw;
+}
+
+// Where key block `cube` lies: how far it extends inside the grid along t, h and w (the block's
+// full size for an interior block) and its first token, or n_tokens for an index outside [0, C).
+struct BlockAt {
+  uint32_t first;
+  int lt, lh, lw;
+};
+template <class BLK>
+__device__ __forceinline__ BlockAt block_at(const Grid3& g, int cube, uint32_t n_tokens) {
+  int bt, bh, bw;
+  cube_coords(g, cube, bt, bh, bw);
+  BlockAt a;
+  a.lt = g.T - BLK::BT * bt;
+  a.lh = g.H - BLK::BH * bh;
+  a.lw = g.W - BLK::BW * bw;
+  a.first = (uint32_t)cube < (uint32_t)g.C ? (uint32_t)((BLK::BT * bt * g.H + BLK::BH * bh) * g.W + BLK::BW * bw)
+                                           : n_tokens;
+  return a;
 }
 
 // ---------------------------------------------------------------- gather + pool
@@ -568,36 +594,38 @@ __device__ __forceinline__ void fine_epilogue(const f32x16* o, float inv, char* 
 // other row of the head, or zeros past its end (range check); those keys are masked before the
 // softmax.  A cube index outside [0, C) starts at the head's end and reads zeros.
 template <int D>
-__device__ __forceinline__ void grid_k_copy(const uint16_t* khead, uint32_t head_bytes, char* kdst, int cube,
+__device__ __forceinline__ void grid_k_copy(const uint16_t* khead, uint32_t head_bytes, char* kdst, const BlockAt& at,
                                             const Grid3& g, int w, int lane) {
   static_assert(D == 128, "16 chunks of 16 bytes per row");
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  const uint32_t first = cube_first_token(cube, g.C, g.nh, g.nw, g.H, g.W, head_bytes / (D * 2));
   const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(khead, head_bytes);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kdst + (i * 2 + w) * 1024), 16,
-                                             (int)grid_k_offset(first, i, w, lane, g.H, g.W), 0, 0, 0);
+                                             (int)grid_k_offset(at.first, i, w, lane, g.H, g.W), 0, 0, 0);
 }
 
 // The same for a V tile from the token grid's V, laid out for transpose reads (VtrSwz): the P V
 // operands are then read as V^T without a transposed copy of V.  Slots outside the grid read
 // zeros (grid_v_offset), as in the cube-ordered copy.
 template <int D>
-__device__ __forceinline__ void grid_v_copy(const uint16_t* vhead, uint32_t head_bytes, char* vdst, int cube,
+__device__ __forceinline__ void grid_v_copy(const uint16_t* vhead, uint32_t head_bytes, char* vdst, const BlockAt& at,
                                             const Grid3& g, int w, int lane) {
   static_assert(D == 128, "16 chunks of 16 bytes per row");
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  const uint32_t first = cube_first_token(cube, g.C, g.nh, g.nw, g.H, g.W, head_bytes / (D * 2));
-  int kt, kh, kw;
-  cube_coords(g, cube, kt, kh, kw);
-  const int lt = g.T - 4 * kt, lh = g.H - 4 * kh, lw = g.W - 4 * kw;
   const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vhead, head_bytes);
+  if (at.lt >= 4 && at.lh >= 4 && at.lw >= 4) {  // an interior cube: every slot is a token
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rv, (lds_ptr)(vdst + (i * 2 + w) * 1024), 16,
-        (int)grid_v_offset(first, i, w, lane, g.H, g.W, lt, lh, lw, head_bytes), 0, 0, 0);
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vdst + (i * 2 + w) * 1024), 16,
+                                               (int)grid_v_offset_full(at.first, i, w, lane, g.H, g.W), 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (lds_ptr)(vdst + (i * 2 + w) * 1024), 16,
+          (int)grid_v_offset(at.first, i, w, lane, g.H, g.W, at.lt, at.lh, at.lw, head_bytes), 0, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------- fine stage
@@ -762,31 +790,31 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   const uint16_t* khead = GRID_QK ? kc + head_row0 * D : kc + cube_base * 64 * D;
   const uint16_t* vhead = GRID_V ? vct + head_row0 * D : vct + cube_base * D * 64;
   // the next K tile: from the cube-ordered copy, or (GRID_QK) from the token grid
-  auto copy_k = [&](int cube) __attribute__((always_inline)) {
+  auto copy_k = [&](int cube, const BlockAt& at) __attribute__((always_inline)) {
     if constexpr (GRID_QK)
-      grid_k_copy<D>(khead, (uint32_t)(N * D * 2), ks, cube, g, wave, lane);
+      grid_k_copy<D>(khead, (uint32_t)(N * D * 2), ks, at, g, wave, lane);
     else
       cube_copy<D, 2>(coff, khead, ks, nullptr, nullptr, cube, g.C, wave);
   };
   // the V tile of a cube: V^T from the cube-ordered copy, or (GRID_V) V from the token grid
-  auto copy_v = [&](int cube) __attribute__((always_inline)) {
+  auto copy_v = [&](int cube, const BlockAt& at) __attribute__((always_inline)) {
     if constexpr (GRID_V)
-      grid_v_copy<D>(vhead, (uint32_t)(N * D * 2), vs, cube, g, wave, lane);
+      grid_v_copy<D>(vhead, (uint32_t)(N * D * 2), vs, at, g, wave, lane);
     else
       cube_copy<D, 2>(coff, nullptr, nullptr, vhead, vs, cube, g.C, wave);
   };
+  // where the current and the next key cube lie (block_at once per cube)
   int cur = plan[0];
-  copy_k(cur);
-  copy_v(cur);
+  BlockAt at_cur = block_at<BLK>(g, cur, (uint32_t)N), at_nxt = at_cur;
+  copy_k(cur, at_cur);
+  copy_v(cur, at_cur);
   wait_tile_copies_keep<VP>();  // K(0) landed; V(0) may still fly
   GatePre gp;
   // masks the padded key slots of an edge block.  Each score is rewritten through a select that
   // reads it: a plain store of -inf into an MFMA result register is a write-after-write the
   // hardware does not order against the MFMA's own late write-back, while a read waits for it.
-  auto mask_keys = [&](int cube) __attribute__((always_inline)) {
-    int kt, kh, kw;
-    cube_coords(g, cube, kt, kh, kw);
-    const int lt = g.T - BLK::BT * kt, lh = g.H - BLK::BH * kh, lw = g.W - BLK::BW * kw;
+  auto mask_keys = [&](const BlockAt& at) __attribute__((always_inline)) {
+    const int lt = at.lt, lh = at.lh, lw = at.lw;
     if (lt < BLK::BT || lh < BLK::BH || lw < BLK::BW) {
       constexpr int PL = BLK::BH * BLK::BW;
 #pragma unroll
@@ -803,8 +831,11 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   barrier_nofence();                                                     // K(0) visible
   mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // S = K(0) Q^T
   barrier_nofence();                                                     // K slot free
-  if (k > 1) copy_k(plan[1]);
-  mask_keys(cur);
+  if (k > 1) {
+    at_nxt = block_at<BLK>(g, plan[1], (uint32_t)N);
+    copy_k(plan[1], at_nxt);
+  }
+  mask_keys(at_cur);
   softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, pa);
   wait_tile_copies();  // K(1) and V(0) landed
   barrier_nofence();   // K(1), V(0) visible
@@ -814,18 +845,21 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   auto tile = [&](int t, auto last_c) __attribute__((always_inline)) {
     constexpr bool LAST = decltype(last_c)::value;
     cur = plan[t];
+    at_cur = at_nxt;
     mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
     wait_tile_copies();  // V(t-1) landed
     barrier_nofence();   // K slot free; V(t-1) visible
     if constexpr (LAST)
       gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
-    else if (t + 1 < k)
-      copy_k(plan[t + 1]);
-    mask_keys(cur);
+    else if (t + 1 < k) {
+      at_nxt = block_at<BLK>(g, plan[t + 1], (uint32_t)N);
+      copy_k(plan[t + 1], at_nxt);
+    }
+    mask_keys(at_cur);
     softmax_tile_pv<D, SM, GRID_V>(vs, pa, s0, s1, sl2, m, l, oacc, pb, j, half);  // O += P(t-1) V(t-1); P(t)
     wait_tile_copies();  // K(t+1) landed (or the gate rows)
     barrier_nofence();   // V slot free; K(t+1) visible
-    copy_v(cur);  // V(t)
+    copy_v(cur, at_cur);  // V(t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) pa[i] = pb[i];
   };
@@ -1035,64 +1069,45 @@ static hipError_t launch_coarse_out(const char* w, const VsaLayout& L, const Gri
   });
 }
 
-// VSA in one call: the gather writes only the cube means and V^T (no cube-ordered Q and K), the
-// coarse scores and top-k fill idx, and the fine stage reads Q and K from the token grid; with a
-// gate, the coarse-branch output and the gated merge as in launch_vsa_fine_gated.
-// The one-call path reads V from the token grid (no transposed copy in the gather, transpose
-// reads in the fine stage) up to this top-k: the copy it saves is a fixed cost per call, the
-// transpose reads and strided V tiles an extra cost per tile (at 480p the call is 3% faster at
-// top-32 and 1% slower at top-78 this way).
-constexpr int kGridVMaxTopk = 48;
-
+// VSA in one call: the gather writes only the cube means (no cube-ordered Q, K or V), the coarse
+// scores and top-k fill idx, and the fine stage reads Q, K and V from the token grid; with a gate,
+// the coarse-branch output and the gated merge as in launch_vsa_fine_gated.
 hipError_t launch_vsa_onecall(const void* q, const void* k, const void* v, int BH, int T, int H, int W, int D,
                               float scale, int topk, int* idx, const void* gate, float* o, float* lse,
                               float* o_coarse, void* ws, hipStream_t s) {
   const Grid3 g = make_grid<Cube>(T, H, W);
   const VsaLayout L = vsa_layout(BH, T, H, W, D);
   char* w = static_cast<char*>(ws);
-  auto vct = reinterpret_cast<uint16_t*>(w + L.vct);
   auto qbar = reinterpret_cast<uint16_t*>(w + L.qbar), kbar = reinterpret_cast<uint16_t*>(w + L.kbar);
   auto vbt = reinterpret_cast<uint16_t*>(w + L.vbt);
   auto qg = static_cast<const uint16_t*>(q), kg = static_cast<const uint16_t*>(k),
        vg = static_cast<const uint16_t*>(v);
-  const bool grid_v = topk <= kGridVMaxTopk;
-  // the means, the mean of V for the coarse branch when there is a gate, Vct unless V is read from
-  // the grid
+  // the means only, and the mean of V for the coarse branch when there is a gate
   auto gather = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(256), 0, s, qg, kg, vg, nullptr, nullptr, vct,
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(256), 0, s, qg, kg, vg, nullptr, nullptr, nullptr,
                        qbar, kbar, vbt, g, 0.0);
   };
   hipError_t e = wf_launch("wf_vsa_gather", s, [&] {
-    if (grid_v) {
-      if (gate) gather(wf_vsa_gather<128, 0, Cube, true, kOutVbar>);
-      else gather(wf_vsa_gather<128, 0, Cube, true, 0>);
-    } else {
-      if (gate) gather(wf_vsa_gather<128, 0, Cube, true, kOutVt | kOutVbar>);
-      else gather(wf_vsa_gather<128, 0, Cube, true, kOutVt>);
-    }
+    if (gate) gather(wf_vsa_gather<128, 0, Cube, true, kOutVbar>);
+    else gather(wf_vsa_gather<128, 0, Cube, true, 0>);
   });
   if (e != hipSuccess) return e;
   e = launch_scores_topk(qbar, kbar, reinterpret_cast<float*>(w + L.scores), nullptr, idx,
                          reinterpret_cast<float2*>(w + L.stat), BH, g, scale, topk, s);
   if (e != hipSuccess) return e;
-  const uint16_t* vsrc = grid_v ? vg : vct;
   auto fine = [&](auto kernel, const uint16_t* gt, const float* oc) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(128), 0, s, qg, kg, vsrc, idx, o, lse, gt, oc, g,
-                       topk, (long)g.C * topk, scale * kLog2e);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * g.C)), dim3(128), 0, s, qg, kg, vg, idx, o, lse, gt, oc, g, topk,
+                       (long)g.C * topk, scale * kLog2e);
   };
-  if (!gate) {
+  if (!gate)
     return wf_launch("wf_vsa_fine", s, [&] {
-      if (grid_v) fine(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Cube, true, true>, nullptr, nullptr);
-      else fine(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Cube, true, false>, nullptr, nullptr);
+      fine(wf_vsa_fine_fwd<128, false, kSoftmaxGuarded, Cube, true, true>, nullptr, nullptr);
     });
-  }
   float* oc = o_coarse ? o_coarse : reinterpret_cast<float*>(w + L.ocoarse);
   e = launch_coarse_out(w, L, g, BH, oc, s);
   if (e != hipSuccess) return e;
-  auto gt = static_cast<const uint16_t*>(gate);
   return wf_launch("wf_vsa_fine_gated", s, [&] {
-    if (grid_v) fine(wf_vsa_fine_fwd<128, true, kSoftmaxGuarded, Cube, true, true>, gt, oc);
-    else fine(wf_vsa_fine_fwd<128, true, kSoftmaxGuarded, Cube, true, false>, gt, oc);
+    fine(wf_vsa_fine_fwd<128, true, kSoftmaxGuarded, Cube, true, true>, static_cast<const uint16_t*>(gate), oc);
   });
 }
 

@@ -9,6 +9,21 @@
 
 namespace wf {
 
+// Division of a block index n < 2^12 by a runtime divisor 1 <= d < 2^20 with one multiply-high:
+// with m = ceil(2^32 / d), n * m / 2^32 exceeds n / d by less than n / 2^32 < 1 / d, so its floor
+// is floor(n / d).  m = 0 stands for d = 1 (whose m needs 33 bits).
+WF_HD constexpr uint32_t div_magic(uint32_t d) {
+  return d <= 1 ? 0u : (uint32_t)(((1ull << 32) + d - 1) / d);
+}
+WF_HD constexpr uint32_t div_by_magic(uint32_t n, uint32_t m) {
+  return m ? (uint32_t)(((uint64_t)n * m) >> 32) : n;
+}
+
+// First token of the cube at cube coordinates (ct, ch, cw) of a T x H x W token grid.
+WF_HD constexpr uint32_t cube_first_token_at(int ct, int ch, int cw, int H, int W) {
+  return (uint32_t)((4 * ct * H + 4 * ch) * W + 4 * cw);
+}
+
 // First token of cube `cube` of the padded (nt, nh, nw) cube grid of a T x H x W token grid
 // (tokens in row-major (t, h, w) order); for an index outside [0, C), N, the head's end.
 WF_HD constexpr uint32_t cube_first_token(int cube, int C, int nh, int nw, int H, int W, uint32_t N) {
@@ -29,16 +44,20 @@ WF_HD constexpr uint32_t grid_k_offset(uint32_t first_token, int i, int w, int l
 }
 
 // The same for a V tile read by transpose reads (VtrSwz): the same pieces and slots, the
-// chunk placed under the V tile's swizzle.  A slot outside the grid (the cube's first lt, lh, lw
+// chunk placed under the V tile's swizzle (grid_v_offset_full, for a cube inside the grid on
+// every axis).  A slot outside the grid (the cube's first lt, lh, lw
 // slot coordinates along t, h, w are inside it) gets head_bytes, which the range check turns
 // into zeros, as the cube-ordered copy holds there: its probability is zero, and a zero row
 // keeps it so whatever the other rows of V hold.
+WF_HD constexpr uint32_t grid_v_offset_full(uint32_t first_token, int i, int w, int lane, int H, int W) {
+  const int sr = 2 * i + w, dw = lane / 16;
+  const uint32_t tok = first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W + dw);
+  return tok * 256u + (uint32_t)VtrSwz::slot(4 * sr + dw, lane % 16) * 16u;
+}
 WF_HD constexpr uint32_t grid_v_offset(uint32_t first_token, int i, int w, int lane, int H, int W, int lt, int lh,
                                        int lw, uint32_t head_bytes) {
   const int sr = 2 * i + w, dw = lane / 16;
-  const uint32_t tok = first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W + dw);
-  return (sr / 4 < lt && sr % 4 < lh && dw < lw) ? tok * 256u + (uint32_t)VtrSwz::slot(4 * sr + dw, lane % 16) * 16u
-                                                   : head_bytes;
+  return (sr / 4 < lt && sr % 4 < lh && dw < lw) ? grid_v_offset_full(first_token, i, w, lane, H, W) : head_bytes;
 }
 
 }  // namespace wf
