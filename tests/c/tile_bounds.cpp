@@ -109,6 +109,11 @@ static void grid_copy(int T, int H, int W) {
                  (unsigned long long)off);
           const uint64_t voff = wf::grid_v_offset(first, i, w, lane, H, W, T - 4 * ct, H - 4 * ch, W - 4 * cw,
                                                    N * 256u);
+          EXPECT((uint64_t)wf::grid_row_part(first, i, w, H, W) + wf::grid_lane_part<false>(i % 2, w, lane) == off,
+                 "grid %dx%dx%d cube %d piece %d w %d lane %d: split K offset differs\n", T, H, W, cube, i, w, lane);
+          EXPECT((uint64_t)wf::grid_row_part(first, i, w, H, W) + wf::grid_lane_part<true>(i % 2, w, lane) ==
+                     wf::grid_v_offset_full(first, i, w, lane, H, W),
+                 "grid %dx%dx%d cube %d piece %d w %d lane %d: split V offset differs\n", T, H, W, cube, i, w, lane);
           if (!(t < T && h < H && x < W))
             EXPECT(voff >= (uint64_t)N * 256, "grid %dx%dx%d cube %d: padded V slot %d is read from memory\n", T, H,
                    W, cube, slot);

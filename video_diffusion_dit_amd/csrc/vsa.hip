@@ -599,10 +599,11 @@ __device__ __forceinline__ void grid_k_copy(const uint16_t* khead, uint32_t head
   static_assert(D == 128, "16 chunks of 16 bytes per row");
   typedef __attribute__((address_space(3))) void* lds_ptr;
   const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(khead, head_bytes);
+  const uint32_t lp[2] = {grid_lane_part<false>(0, w, lane), grid_lane_part<false>(1, w, lane)};
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kdst + (i * 2 + w) * 1024), 16,
-                                             (int)grid_k_offset(at.first, i, w, lane, g.H, g.W), 0, 0, 0);
+                                             (int)(grid_row_part(at.first, i, w, g.H, g.W) + lp[i % 2]), 0, 0, 0);
 }
 
 // The same for a V tile from the token grid's V, laid out for transpose reads (VtrSwz): the P V
@@ -615,10 +616,11 @@ __device__ __forceinline__ void grid_v_copy(const uint16_t* vhead, uint32_t head
   typedef __attribute__((address_space(3))) void* lds_ptr;
   const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vhead, head_bytes);
   if (at.lt >= 4 && at.lh >= 4 && at.lw >= 4) {  // an interior cube: every slot is a token
+    const uint32_t lp[2] = {grid_lane_part<true>(0, w, lane), grid_lane_part<true>(1, w, lane)};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(vdst + (i * 2 + w) * 1024), 16,
-                                               (int)grid_v_offset_full(at.first, i, w, lane, g.H, g.W), 0, 0, 0);
+                                               (int)(grid_row_part(at.first, i, w, g.H, g.W) + lp[i % 2]), 0, 0, 0);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -641,28 +643,26 @@ __device__ __forceinline__ void grid_v_copy(const uint16_t* vhead, uint32_t head
 // ends by reading the last MFMA's result, which waits for the matrix pipe to
 // drain before any later instruction may reuse those registers.  Returns the
 // lane's sum of the new probabilities, summed in tile_probs' order.
-template <int D, bool VTR = false>
+template <int D, bool VTR>
 __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_old, f32x16* o, const f32x16& s0,
-                                               const f32x16& s1, float sl2, float m, bf16x2* p_new, int j,
-                                               int half) {
+                                               const f32x16& s1, float sl2, float m, bf16x2* p_new,
+                                               const OperandTable<D, VTR>& tb) {
   constexpr int NPV = Pairs<D>::NPV, PF = kRingPF, R = kRing;
   static_assert(NPV == 16 && D == 128, "one probability pair per P V MFMA");
-  OperandBase<D, VTR> ob(j, half);
-  asm volatile("" : "+v"(ob.k), "+v"(ob.v));
   bf16x8 pg[4];  // B operand of the k-step ks: probabilities 4 ks .. 4 ks + 3
 #pragma unroll
   for (int g = 0; g < 4; ++g)
     pg[g] = __builtin_bit_cast(bf16x8, P4{p_old[4 * g], p_old[4 * g + 1], p_old[4 * g + 2], p_old[4 * g + 3]});
   uint4 ring[R];
 #pragma unroll
-  for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D, VTR>(u, vt, nullptr, ob);
+  for (int u = 0; u < PF; ++u) ring[u] = table_operand<D, VTR>(u, vt, nullptr, tb);
   const float nm = -m;
   const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
   float la = 0.f, lb = 0.f;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
-    if (i + PF < NPV) ring[(i + PF) % R] = mfma_operand<D, VTR>(i + PF, vt, nullptr, ob);
+    if (i + PF < NPV) ring[(i + PF) % R] = table_operand<D, VTR>(i + PF, vt, nullptr, tb);
     __builtin_amdgcn_sched_barrier(0);
     const f32x16& sv = i < 8 ? s0 : s1;
     const int r = i % 8;
@@ -690,21 +690,21 @@ __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_o
 // softmax_tile for tile t with P(t-1) V(t-1) run inside it (pv_with_probs).
 // The arithmetic is softmax_tile's, in the same order relative to O: P V of
 // tile t-1 is accumulated before O is rescaled for tile t's reference.
-template <int D, int SM, bool VTR = false>
+template <int D, int SM, bool VTR>
 __device__ __forceinline__ void softmax_tile_pv(const char* vt, const bf16x2* p_old, const f32x16& s0,
                                                 const f32x16& s1, float sl2, float& m, float& l, f32x16* o,
-                                                bf16x2* p_new, int j, int half) {
+                                                bf16x2* p_new, const OperandTable<D, VTR>& tb) {
   constexpr int DB = D / 32;
   if constexpr (SM == kSoftmaxRunningMax) {
     const float mnew = fmaxf(m, tile_row_max(s0, s1, sl2));
-    const float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, mnew, p_new, j, half);
+    const float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, mnew, p_new, tb);
     rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
     m = mnew;
     l += lt;
   } else if constexpr (SM == kSoftmaxFixedFirst) {
-    l += pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
+    l += pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, tb);
   } else {
-    float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, j, half);
+    float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, tb);
     if (__ballot(!(lt <= 0x1p16f))) {  // a big jump (the first tile is not run here)
       const float mnew = fmaxf(m, ceilf(tile_row_max(s0, s1, sl2)));
       rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
@@ -785,6 +785,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
 
   const CopyOffsets<D, 2> coff(wave, lane, 64);
   constexpr int VP = CopyOffsets<D, 2>::VPW;  // V^T copies per wavefront and tile
+  const OperandTable<D, GRID_V> otab(j, half);  // every operand read's LDS offset
   // the head's cube-ordered K and V^T: every copy is range-checked against these C cubes, so a
   // plan entry outside [0, C) reads zeros (cube_copy) instead of memory beyond them
   const uint16_t* khead = GRID_QK ? kc + head_row0 * D : kc + cube_base * 64 * D;
@@ -829,7 +830,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   };
   // tile 0: scores and probabilities (its P V runs inside tile 1's softmax)
   barrier_nofence();                                                     // K(0) visible
-  mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // S = K(0) Q^T
+  mfma_run_t<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(0) Q^T
   barrier_nofence();                                                     // K slot free
   if (k > 1) {
     at_nxt = block_at<BLK>(g, plan[1], (uint32_t)N);
@@ -846,7 +847,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     constexpr bool LAST = decltype(last_c)::value;
     cur = plan[t];
     at_cur = at_nxt;
-    mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // S = K(t) Q^T
+    mfma_run_t<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(t) Q^T
     wait_tile_copies();  // V(t-1) landed
     barrier_nofence();   // K slot free; V(t-1) visible
     if constexpr (LAST)
@@ -856,7 +857,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
       copy_k(plan[t + 1], at_nxt);
     }
     mask_keys(at_cur);
-    softmax_tile_pv<D, SM, GRID_V>(vs, pa, s0, s1, sl2, m, l, oacc, pb, j, half);  // O += P(t-1) V(t-1); P(t)
+    softmax_tile_pv<D, SM, GRID_V>(vs, pa, s0, s1, sl2, m, l, oacc, pb, otab);  // O += P(t-1) V(t-1); P(t)
     wait_tile_copies();  // K(t+1) landed (or the gate rows)
     barrier_nofence();   // V slot free; K(t+1) visible
     copy_v(cur, at_cur);  // V(t)
@@ -874,7 +875,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   if constexpr (GATED) {  // a single tile had no later tile to load them in
     if (k == 1) gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
   }
-  mfma_run<D, 0, NPV, GRID_V>(vs, ks, pa, qop, oacc, s0, s1, j, half);  // O += P(k-1) V(k-1)
+  mfma_run_t<D, 0, NPV>(vs, ks, pa, qop, oacc, s0, s1, otab);  // O += P(k-1) V(k-1)
   wait_tile_copies();  // the gate rows (k = 1)
   barrier_nofence();   // every wavefront is done with both slots
   const float lt = l + __shfl_xor(l, 32);

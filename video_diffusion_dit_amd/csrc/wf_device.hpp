@@ -221,6 +221,49 @@ __device__ __forceinline__ uint4 mfma_operand(int i, const char* vt, const char*
   return *reinterpret_cast<const uint4*>(kt + kb * 32 * D * 2 + (ob.k ^ (uint32_t)(32 * kk)));
 }
 
+// The per-lane LDS offsets of every operand read of a tile, computed once and kept in registers
+// (loop invariant), so a read costs no address arithmetic: K k-step kk reads at k[kk] (the 32-row
+// block is an immediate); a V^T read of key step ks at v[ks] (the 32-row block is an immediate),
+// or, with VTR, transpose read r of dim block b at v[2 b + r] (the key step's rows are an
+// immediate).
+template <int D, bool VTR>
+struct OperandTable {
+  static constexpr int NV = VTR ? 8 : 4;
+  uint32_t k[D / 16], v[NV];
+  __device__ __forceinline__ OperandTable(int j, int half) {
+    const OperandBase<D, VTR> ob(j, half);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) k[kk] = ob.k ^ (uint32_t)(32 * kk);
+#pragma unroll
+    for (int x = 0; x < NV; ++x) v[x] = VTR ? (ob.v ^ (uint32_t)((4 * (x / 2) + 2 * (x % 2)) * 16)) : (ob.v ^ (uint32_t)(32 * x));
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(k[kk]));
+#pragma unroll
+    for (int x = 0; x < NV; ++x) asm volatile("" : "+v"(v[x]));
+  }
+};
+
+template <int D, bool VTR>
+__device__ __forceinline__ uint4 table_operand(int i, const char* vt, const char* kt, const OperandTable<D, VTR>& tb) {
+  constexpr int NPV = Pairs<D>::NPV;
+  if (i < NPV) {
+    const int ks = i / (D / 32), b = i % (D / 32);
+    if constexpr (VTR) {
+      static_assert(D == 128, "V tile rows of 256 bytes");
+      typedef short s4 __attribute__((ext_vector_type(4)));
+      typedef short s8 __attribute__((ext_vector_type(8)));
+      typedef __attribute__((address_space(3))) s4* lds_s4;
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vt + tb.v[2 * b] + 16 * ks * 256));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vt + tb.v[2 * b + 1] + (16 * ks + 8) * 256));
+      return __builtin_bit_cast(uint4, (s8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return *reinterpret_cast<const uint4*>(vt + b * 32 * 128 + tb.v[ks]);
+    }
+  }
+  const int kk = (i - NPV) / 2, kb = (i - NPV) % 2;
+  return *reinterpret_cast<const uint4*>(kt + kb * 32 * D * 2 + tb.k[kk]);
+}
+
 template <int D>
 __device__ __forceinline__ void mfma_pair(int i, uint4 a, const bf16x2* p2, const bf16x8* qop, f32x16* o,
                                           f32x16& s0, f32x16& s1) {
@@ -284,6 +327,28 @@ __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const b
                                          f32x16* o, f32x16& s0, f32x16& s1, int j, int half) {
   uint4 ring[kRing];
   mfma_run<D, I0, I1, false, VTR>(vt, kt, p2, qop, o, s0, s1, j, half, ring);
+}
+
+// mfma_run with the operand offsets from an OperandTable.
+template <int D, int I0, int I1, bool VTR>
+__device__ __forceinline__ void mfma_run_t(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
+                                           f32x16* o, f32x16& s0, f32x16& s1, const OperandTable<D, VTR>& tb) {
+  constexpr int PF = kRingPF, R = kRing, NP = I1 - I0;
+  static_assert(NP >= PF, "run shorter than the prefetch distance");
+  if constexpr (I1 > Pairs<D>::NPV) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+  }
+  uint4 ring[R];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) ring[u] = table_operand<D, VTR>(I0 + u, vt, kt, tb);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (i + PF < NP) ring[(i + PF) % R] = table_operand<D, VTR>(I0 + i + PF, vt, kt, tb);
+    mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // ------------------------------------------------------------- softmax tile

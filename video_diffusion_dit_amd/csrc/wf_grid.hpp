@@ -49,6 +49,21 @@ WF_HD constexpr uint32_t grid_k_offset(uint32_t first_token, int i, int w, int l
 // slot coordinates along t, h, w are inside it) gets head_bytes, which the range check turns
 // into zeros, as the cube-ordered copy holds there: its probability is zero, and a zero row
 // keeps it so whatever the other rows of V hold.
+// The same offsets split into a part shared by the wavefront and a per-lane part, so a copy
+// costs one add per piece: piece i of wavefront w starts at token row part grid_row_part and lane
+// `lane` adds grid_lane_part (which depends on i only through i % 2; V selects the V tile's
+// swizzle).  grid_row_part(...) + grid_lane_part<V>(i % 2, ...) equals grid_k_offset (V: the
+// in-grid grid_v_offset).
+WF_HD constexpr uint32_t grid_row_part(uint32_t first_token, int i, int w, int H, int W) {
+  const int sr = 2 * i + w;
+  return (first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W)) * 256u;
+}
+template <bool V>
+WF_HD constexpr uint32_t grid_lane_part(int i_odd, int w, int lane) {
+  const int dw = lane / 16, row = 4 * (2 * i_odd + w) + dw;  // the slot row modulo 16
+  return (uint32_t)dw * 256u + (uint32_t)(V ? VtrSwz::slot(row, lane % 16) : Swz<128>::kslot(row, lane % 16)) * 16u;
+}
+
 WF_HD constexpr uint32_t grid_v_offset_full(uint32_t first_token, int i, int w, int lane, int H, int W) {
   const int sr = 2 * i + w, dw = lane / 16;
   const uint32_t tok = first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W + dw);
