@@ -54,7 +54,8 @@ __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict
 // the slot K(t-1) left and half B copies V(t+2) into the slot V(t-1) left, so
 // the copy work is split evenly over the two halves; each waits for its copies
 // at the end of its next MFMA phase, so each copy has a phase to land.  Within an MFMA phase the
-// LDS operand reads run four MFMAs ahead of use; the first four are read early in
+// LDS operand reads run four MFMAs ahead of use, at offsets precomputed once per workgroup
+// (OperandTable: 12 registers that save an address computation per read); the first four are read early in
 // the wavefront's VALU phase, right after its copies, so their latency hides behind the
 // softmax.  SM selects the
 // softmax reference policy (softmax_tile; the library default is the guarded
@@ -129,12 +130,13 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // VALU phase (V(t) was published by the barrier that opened it), so the matrix pipe does not
   // idle through the LDS latency at each phase start and the reads overlap the softmax.
   uint4 ring[kRing];
+  const OperandTable<D, false> otab(j, half);  // every operand read's LDS offset
   auto phase_pair = [&](auto half_a_c, int t, const char* kcur, const char* vprev, char* knext,
                         const char* vnext) __attribute__((always_inline)) {
     constexpr bool HALF_A = decltype(half_a_c)::value;  // half A copies K tiles, half B V^T tiles
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);  // MFMA phase first at the SIMD's issue arbiter
-    mfma_run<D, 0, Pairs<D>::NPV + Pairs<D>::NQK, true>(vprev, kcur, p2, qop, oacc, s0, s1, j, half, ring);
+    mfma_run<D, 0, Pairs<D>::NPV + Pairs<D>::NQK, true>(vprev, kcur, p2, qop, oacc, s0, s1, otab, ring);
     __builtin_amdgcn_s_setprio(0);
     wait_tile_copies();  // half A: K(t+1) landed; half B: V(t+1) landed
     barrier_nofence();
@@ -147,7 +149,7 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     else
       tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + (long)(t + 2) * 64, Np,
                       t + 2 < nt ? vbytes - (uint32_t)(t + 2) * 128 : 0u, const_cast<char*>(vprev), wq);
-    mfma_prefill<D, 0>(ring, vnext, kcur, j, half);  // first operands of MFMA phase t+1: V(t) rows
+    mfma_prefill<D, 0>(ring, vnext, kcur, otab);  // first operands of MFMA phase t+1: V(t) rows
     if (t < nt) {
       if ((t + 1) * 64 > N) {  // ragged last tile: keys >= N do not exist
         // selects that read the scores: a plain store into an MFMA result register is not
@@ -165,7 +167,7 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // unrolled by three so every LDS array is named statically, and instantiated once per half
   // (half A or B) so the compiler tracks the copies on straight-line paths
   auto tile_loop = [&](auto half_a_c) __attribute__((always_inline)) {
-    mfma_prefill<D, 0>(ring, vt2, kt0, j, half);  // MFMA phase 0: V(-1), the zero slot
+    mfma_prefill<D, 0>(ring, vt2, kt0, otab);  // MFMA phase 0: V(-1), the zero slot
     for (int t = 0; t <= nt; t += 3) {
       phase_pair(half_a_c, t, kt0, vt2, kt2, vt0);
       if (t + 1 <= nt) {  // nested, so every path into a phase passes the previous phase's wait

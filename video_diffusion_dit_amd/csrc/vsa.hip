@@ -830,7 +830,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   };
   // tile 0: scores and probabilities (its P V runs inside tile 1's softmax)
   barrier_nofence();                                                     // K(0) visible
-  mfma_run_t<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(0) Q^T
+  mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(0) Q^T
   barrier_nofence();                                                     // K slot free
   if (k > 1) {
     at_nxt = block_at<BLK>(g, plan[1], (uint32_t)N);
@@ -847,7 +847,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
     constexpr bool LAST = decltype(last_c)::value;
     cur = plan[t];
     at_cur = at_nxt;
-    mfma_run_t<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(t) Q^T
+    mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(t) Q^T
     wait_tile_copies();  // V(t-1) landed
     barrier_nofence();   // K slot free; V(t-1) visible
     if constexpr (LAST)
@@ -875,7 +875,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   if constexpr (GATED) {  // a single tile had no later tile to load them in
     if (k == 1) gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
   }
-  mfma_run_t<D, 0, NPV>(vs, ks, pa, qop, oacc, s0, s1, otab);  // O += P(k-1) V(k-1)
+  mfma_run<D, 0, NPV>(vs, ks, pa, qop, oacc, s0, s1, otab);  // O += P(k-1) V(k-1)
   wait_tile_copies();  // the gate rows (k = 1)
   barrier_nofence();   // every wavefront is done with both slots
   const float lt = l + __shfl_xor(l, 32);

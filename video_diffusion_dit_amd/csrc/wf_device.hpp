@@ -181,11 +181,8 @@ struct Pairs {
 // (s = k-step) the swizzled chunk is (2 s + half) ^ f(row) = 2 s ^ (half ^ f(row)),
 // and the row's byte offset has zero bits where the chunk lives, so every
 // operand address is one per-lane base XOR 32 s plus an immediate (the tile,
-// and the 32-row block).  The bases are made opaque once per run so the
-// compiler computes the XORs in place instead of keeping one register per
-// k-step alive across the loop.
-// With VTR the V operand comes from a V tile ([keys][D], VtrSwz) through two
-// transpose reads instead of one read of a V^T tile.
+// and the 32-row block).  With VTR the V operand comes from a V tile ([keys][D],
+// VtrSwz) through two transpose reads instead of one read of a V^T tile.
 template <int D, bool VTR = false>
 struct OperandBase {
   uint32_t k, v;
@@ -196,33 +193,9 @@ struct OperandBase {
   }
 };
 
-// V operand of P V pair (ks, b) from a V tile: transpose reads r = 0 and 1 give elements 0..3 and
-// 4..7 (keys 16 ks + 8 r + 4 half + 0..3 of dim 32 b + j).
-template <int D>
-__device__ __forceinline__ uint4 vtr_operand(const char* v, uint32_t base, int ks, int b) {
-  static_assert(D == 128, "V tile rows of 256 bytes");
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  typedef short s8 __attribute__((ext_vector_type(8)));
-  typedef __attribute__((address_space(3))) s4* lds_s4;
-  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(v + VtrSwz::offset(base, ks, b, 0)));
-  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(v + VtrSwz::offset(base, ks, b, 1)));
-  return __builtin_bit_cast(uint4, (s8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-template <int D, bool VTR = false>
-__device__ __forceinline__ uint4 mfma_operand(int i, const char* vt, const char* kt, const OperandBase<D, VTR>& ob) {
-  constexpr int NPV = Pairs<D>::NPV;
-  if (i < NPV) {  // ks = i / (D/32), block b = i % (D/32): V^T rows b*32 + j
-    const int ks = i / (D / 32), b = i % (D / 32);
-    if constexpr (VTR) return vtr_operand<D>(vt, ob.v, ks, b);
-    return *reinterpret_cast<const uint4*>(vt + b * 32 * 128 + (ob.v ^ (uint32_t)(32 * ks)));
-  }
-  const int kk = (i - NPV) / 2, kb = (i - NPV) % 2;  // K rows kb*32 + j
-  return *reinterpret_cast<const uint4*>(kt + kb * 32 * D * 2 + (ob.k ^ (uint32_t)(32 * kk)));
-}
-
 // The per-lane LDS offsets of every operand read of a tile, computed once and kept in registers
-// (loop invariant), so a read costs no address arithmetic: K k-step kk reads at k[kk] (the 32-row
+// (loop invariant; 12 registers for D = 128, 16 with VTR), so a read costs no address
+// arithmetic -- 1.4% of the dense kernel's time and 1-2% of the VSA fine stage's: K k-step kk reads at k[kk] (the 32-row
 // block is an immediate); a V^T read of key step ks at v[ks] (the 32-row block is an immediate),
 // or, with VTR, transpose read r of dim block b at v[2 b + r] (the key step's rows are an
 // immediate).
@@ -289,59 +262,27 @@ __device__ __forceinline__ void mfma_pair(int i, uint4 a, const bf16x2* p2, cons
 // so the run starts its first MFMA without waiting for LDS).
 constexpr int kRingPF = 4, kRing = kRingPF + 1;
 
-template <int D, int I0, bool VTR = false>
-__device__ __forceinline__ void mfma_prefill(uint4 (&ring)[kRing], const char* vt, const char* kt, int j, int half) {
-  OperandBase<D, VTR> ob(j, half);
-  asm volatile("" : "+v"(ob.k), "+v"(ob.v));
+template <int D, int I0, bool VTR>
+__device__ __forceinline__ void mfma_prefill(uint4 (&ring)[kRing], const char* vt, const char* kt,
+                                               const OperandTable<D, VTR>& tb) {
 #pragma unroll
-  for (int u = 0; u < kRingPF; ++u) ring[u] = mfma_operand<D, VTR>(I0 + u, vt, kt, ob);
+  for (int u = 0; u < kRingPF; ++u) ring[u] = table_operand<D, VTR>(I0 + u, vt, kt, tb);
 }
 
-template <int D, int I0, int I1, bool PREFILLED = false, bool VTR = false>
+template <int D, int I0, int I1, bool PREFILLED, bool VTR>
 __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
-                                         f32x16* o, f32x16& s0, f32x16& s1, int j, int half,
-                                         uint4 (&ring)[kRing]) {
+                                           f32x16* o, f32x16& s0, f32x16& s1, const OperandTable<D, VTR>& tb,
+                                           uint4 (&ring)[kRing]) {
   constexpr int PF = kRingPF, R = kRing, NP = I1 - I0;
   static_assert(NP >= PF, "run shorter than the prefetch distance");
   if constexpr (I1 > Pairs<D>::NPV) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
   }
-  OperandBase<D, VTR> ob(j, half);
-  asm volatile("" : "+v"(ob.k), "+v"(ob.v));
   if constexpr (!PREFILLED) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) ring[u] = mfma_operand<D, VTR>(I0 + u, vt, kt, ob);
+    for (int u = 0; u < PF; ++u) ring[u] = table_operand<D, VTR>(I0 + u, vt, kt, tb);
   }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    if (i + PF < NP) ring[(i + PF) % R] = mfma_operand<D, VTR>(I0 + i + PF, vt, kt, ob);
-    mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-template <int D, int I0, int I1, bool VTR = false>
-__device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
-                                         f32x16* o, f32x16& s0, f32x16& s1, int j, int half) {
-  uint4 ring[kRing];
-  mfma_run<D, I0, I1, false, VTR>(vt, kt, p2, qop, o, s0, s1, j, half, ring);
-}
-
-// mfma_run with the operand offsets from an OperandTable.
-template <int D, int I0, int I1, bool VTR>
-__device__ __forceinline__ void mfma_run_t(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
-                                           f32x16* o, f32x16& s0, f32x16& s1, const OperandTable<D, VTR>& tb) {
-  constexpr int PF = kRingPF, R = kRing, NP = I1 - I0;
-  static_assert(NP >= PF, "run shorter than the prefetch distance");
-  if constexpr (I1 > Pairs<D>::NPV) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-  }
-  uint4 ring[R];
-#pragma unroll
-  for (int u = 0; u < PF; ++u) ring[u] = table_operand<D, VTR>(I0 + u, vt, kt, tb);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -349,6 +290,13 @@ __device__ __forceinline__ void mfma_run_t(const char* vt, const char* kt, const
     mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+template <int D, int I0, int I1, bool VTR>
+__device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
+                                           f32x16* o, f32x16& s0, f32x16& s1, const OperandTable<D, VTR>& tb) {
+  uint4 ring[kRing];
+  mfma_run<D, I0, I1, false, VTR>(vt, kt, p2, qop, o, s0, s1, tb, ring);
 }
 
 // ------------------------------------------------------------- softmax tile
