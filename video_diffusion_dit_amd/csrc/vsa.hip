@@ -126,7 +126,7 @@ __device__ __forceinline__ BlockAt block_at(const Grid3& g, int cube, uint32_t n
   a.lt = g.T - BLK::BT * bt;
   a.lh = g.H - BLK::BH * bh;
   a.lw = g.W - BLK::BW * bw;
-  a.first = (uint32_t)cube < (uint32_t)g.C ? (uint32_t)((BLK::BT * bt * g.H + BLK::BH * bh) * g.W + BLK::BW * bw)
+  a.first = (uint32_t)cube < (uint32_t)g.C ? block_first_token<BLK::BT, BLK::BH, BLK::BW>(bt, bh, bw, g.H, g.W)
                                            : n_tokens;
   return a;
 }

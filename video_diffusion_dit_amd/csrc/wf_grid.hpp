@@ -19,9 +19,14 @@ WF_HD constexpr uint32_t div_by_magic(uint32_t n, uint32_t m) {
   return m ? (uint32_t)(((uint64_t)n * m) >> 32) : n;
 }
 
-// First token of the cube at cube coordinates (ct, ch, cw) of a T x H x W token grid.
+// First token of the BT x BH x BW block at block coordinates (bt, bh, bw) of a T x H x W token
+// grid; cube_first_token_at for 4x4x4 cubes.
+template <int BT, int BH, int BW>
+WF_HD constexpr uint32_t block_first_token(int bt, int bh, int bw, int H, int W) {
+  return (uint32_t)((BT * bt * H + BH * bh) * W + BW * bw);
+}
 WF_HD constexpr uint32_t cube_first_token_at(int ct, int ch, int cw, int H, int W) {
-  return (uint32_t)((4 * ct * H + 4 * ch) * W + 4 * cw);
+  return block_first_token<4, 4, 4>(ct, ch, cw, H, W);
 }
 
 // First token of cube `cube` of the padded (nt, nh, nw) cube grid of a T x H x W token grid
