@@ -1,6 +1,7 @@
-// Offsets of the key-tile copies that read one 4x4x4 key cube of K and V straight from the token
-// grid (the one-call VSA path, which skips the cube-ordered copies of K and V).  Plain C++ for host and
-// device, so the arithmetic can be checked on the host.
+// Block arithmetic of the VSA path: block coordinates by multiply-high division, first tokens of
+// blocks, and the offsets of the copies that read one 4x4x4 key cube of K and V straight from the
+// token grid (the one-call path, which skips the cube-ordered copies of K and V).  Plain C++ for
+// host and device, so the arithmetic can be checked on the host.
 #pragma once
 
 #include <stdint.h>
@@ -48,17 +49,11 @@ WF_HD constexpr uint32_t grid_k_offset(uint32_t first_token, int i, int w, int l
   return tok * 256u + (uint32_t)Swz<128>::kslot(4 * sr + dw, lane % 16) * 16u;
 }
 
-// The same for a V tile read by transpose reads (VtrSwz): the same pieces and slots, the
-// chunk placed under the V tile's swizzle (grid_v_offset_full, for a cube inside the grid on
-// every axis).  A slot outside the grid (the cube's first lt, lh, lw
-// slot coordinates along t, h, w are inside it) gets head_bytes, which the range check turns
-// into zeros, as the cube-ordered copy holds there: its probability is zero, and a zero row
-// keeps it so whatever the other rows of V hold.
 // The same offsets split into a part shared by the wavefront and a per-lane part, so a copy
 // costs one add per piece: piece i of wavefront w starts at token row part grid_row_part and lane
-// `lane` adds grid_lane_part (which depends on i only through i % 2; V selects the V tile's
-// swizzle).  grid_row_part(...) + grid_lane_part<V>(i % 2, ...) equals grid_k_offset (V: the
-// in-grid grid_v_offset).
+// `lane` adds grid_lane_part, which depends on i only through i % 2 (V selects the V tile's
+// swizzle, VtrSwz).  grid_row_part(...) + grid_lane_part<false>(i % 2, ...) equals
+// grid_k_offset, and with <true> grid_v_offset_full.
 WF_HD constexpr uint32_t grid_row_part(uint32_t first_token, int i, int w, int H, int W) {
   const int sr = 2 * i + w;
   return (first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W)) * 256u;
@@ -69,11 +64,16 @@ WF_HD constexpr uint32_t grid_lane_part(int i_odd, int w, int lane) {
   return (uint32_t)dw * 256u + (uint32_t)(V ? VtrSwz::slot(row, lane % 16) : Swz<128>::kslot(row, lane % 16)) * 16u;
 }
 
+// grid_k_offset for a V tile read by transpose reads: the same pieces and slots, the chunk placed
+// under the V tile's swizzle (VtrSwz) -- for a cube inside the grid on every axis.
 WF_HD constexpr uint32_t grid_v_offset_full(uint32_t first_token, int i, int w, int lane, int H, int W) {
   const int sr = 2 * i + w, dw = lane / 16;
   const uint32_t tok = first_token + (uint32_t)((sr / 4) * H * W + (sr % 4) * W + dw);
   return tok * 256u + (uint32_t)VtrSwz::slot(4 * sr + dw, lane % 16) * 16u;
 }
+// The same for any cube: a slot outside the grid (the cube extends lt, lh, lw slots inside it
+// along t, h, w) gets head_bytes, which the range check turns into zeros, as the cube-ordered copy
+// holds there -- its probability is zero, and a zero row keeps it so whatever V holds elsewhere.
 WF_HD constexpr uint32_t grid_v_offset(uint32_t first_token, int i, int w, int lane, int H, int W, int lt, int lh,
                                        int lw, uint32_t head_bytes) {
   const int sr = 2 * i + w, dw = lane / 16;
