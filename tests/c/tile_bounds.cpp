@@ -9,6 +9,8 @@
 //    and for a cube index outside [0, C) starts at the head's end; its V copy reads the same
 //    token rows, chunks placed under the V tile's swizzle (VtrSwz);
 //  * block coordinates by multiply-high division (div_magic) match plain division;
+//  * second_half_padded, which lets the fine stage skip work on edge blocks, holds exactly when
+//    slots 32..63 are all padding;
 //  * the transpose reads of that V tile (VtrSwz offsets, under the lane mapping of gfx950's
 //    ds_read_b64_tr_b16) deliver to every lane of every P V MFMA exactly the V^T elements its A
 //    operand needs, in the probability registers' key order, and each half wavefront of every
@@ -201,7 +203,24 @@ static void magic_division() {
   }
 }
 
+// second_half_padded against the slot layout itself, for both block shapes and every extent of a
+// block along each axis (an edge block's 1 .. B-1 tokens, or a whole one).
+template <int BT, int BH, int BW>
+static void half_padding() {
+  for (int lt = 1; lt <= BT + 2; ++lt)
+    for (int lh = 1; lh <= BH + 2; ++lh)
+      for (int lw = 1; lw <= BW + 2; ++lw) {
+        bool all = true;
+        for (int s = 32; s < 64; ++s)
+          if (s / (BH * BW) < lt && (s / BW) % BH < lh && s % BW < lw) all = false;
+        const bool got = wf::second_half_padded<BT, BH, BW>(lt, lh);
+        EXPECT(got == all, "block %dx%dx%d extents %d,%d,%d: %d, want %d\n", BT, BH, BW, lt, lh, lw, (int)got, (int)all);
+      }
+}
+
 int main() {
+  half_padding<4, 4, 4>();
+  half_padding<1, 8, 8>();
   magic_division();
   transpose_reads();
   coverage<128, 2>();

@@ -68,7 +68,7 @@ def check_heads(wl, q, k, v, gate, g, tok, heads, cubes=None):
 
 @pytest.mark.parametrize("grid,topk,B,Hh", [((5, 6, 7), 3, 1, 2), ((9, 10, 11), 5, 2, 1),
                                             ((4, 4, 4), 1, 1, 1), ((1, 1, 1), 1, 1, 1),
-                                            ((13, 6, 21), 17, 1, 2), ((3, 17, 9), 2, 1, 1)])
+                                            ((13, 6, 21), 17, 1, 2), ((3, 17, 9), 2, 1, 1), ((10, 9, 14), 6, 1, 1)])
 def test_vsa_gated_small_grids(wf, grid, topk, B, Hh):
     T, H, W = grid
     wl = synth.small_workload("vsa_gated", B, Hh, T, H, W, 128, structured=True,

@@ -131,6 +131,13 @@ __device__ __forceinline__ BlockAt block_at(const Grid3& g, int cube, uint32_t n
   return a;
 }
 
+// Whether keys (or query slots) 32..63 of block `a` are all padding: the second score block of a
+// key tile (its probabilities are zero) or the second wavefront's query rows.
+template <class BLK>
+__device__ __forceinline__ bool upper_half_padded(const BlockAt& a) {
+  return second_half_padded<BLK::BT, BLK::BH, BLK::BW>(a.lt, a.lh);
+}
+
 // ---------------------------------------------------------------- gather + pool
 // One workgroup per (bh, block).  Writes Qc, Kc [BH][C][64][D] (padded slots
 // zero), Vct [BH][C][D][64] (slots in perm16 order) and, with POOL, the fp32
@@ -643,10 +650,20 @@ __device__ __forceinline__ void grid_v_copy(const uint16_t* vhead, uint32_t head
 // ends by reading the last MFMA's result, which waits for the matrix pipe to
 // drain before any later instruction may reuse those registers.  Returns the
 // lane's sum of the new probabilities, summed in tile_probs' order.
+//
+// Keys 32..63 of an edge block may all be padding (upper_half_padded): their
+// probabilities are then zero.  hv (uniform over the wavefront) says the
+// previous tile was such a block: its P V pairs 8..15, which would add zeros,
+// are skipped by scalar branches, one per step (a single branch between two
+// copies of steps 8..15 costs the kernel its register budget); a caller that
+// passes a constant false gets no branches.  Each probability pair is pinned
+// to its step (an empty asm on the sum it feeds): with branches in the
+// sequence the compiler would otherwise sink the pairs that only feed a sum
+// past them and bunch them up, away from the MFMAs they are meant to overlap.
 template <int D, bool VTR>
 __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_old, f32x16* o, const f32x16& s0,
                                                const f32x16& s1, float sl2, float m, bf16x2* p_new,
-                                               const OperandTable<D, VTR>& tb) {
+                                               const OperandTable<D, VTR>& tb, bool hv) {
   constexpr int NPV = Pairs<D>::NPV, PF = kRingPF, R = kRing;
   static_assert(NPV == 16 && D == 128, "one probability pair per P V MFMA");
   bf16x8 pg[4];  // B operand of the k-step ks: probabilities 4 ks .. 4 ks + 3
@@ -669,11 +686,18 @@ __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_o
     p_new[i] = __builtin_convertvector((f32x2){__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * r], sl2, nm)),
                                                __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * r + 1], sl2, nm))},
                                        bf16x2);
-    if (i % 2 == 0) la = __builtin_amdgcn_fdot2_f32_bf16(p_new[i], one2, la, false);
-    else lb = __builtin_amdgcn_fdot2_f32_bf16(p_new[i], one2, lb, false);
+    if (i % 2 == 0) {
+      la = __builtin_amdgcn_fdot2_f32_bf16(p_new[i], one2, la, false);
+      asm volatile("" : "+v"(la));
+    } else {
+      lb = __builtin_amdgcn_fdot2_f32_bf16(p_new[i], one2, lb, false);
+      asm volatile("" : "+v"(lb));
+    }
     __builtin_amdgcn_sched_barrier(0);
-    const int ks = i / 4, b = i % 4;  // mfma_pair's numbering of the P V pairs
-    o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ring[i % R]), pg[ks], o[b], 0, 0, 0);
+    if (i < 8 || !hv) {
+      const int ks = i / 4, b = i % 4;  // mfma_pair's numbering of the P V pairs
+      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ring[i % R]), pg[ks], o[b], 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -681,9 +705,9 @@ __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_o
   asm volatile("" ::"v"(v4(pg[0])), "v"(v4(pg[1])), "v"(v4(pg[2])), "v"(v4(pg[3])), "v"(v4(ring[0])),
                "v"(v4(ring[1])), "v"(v4(ring[2])), "v"(v4(ring[3])), "v"(v4(ring[4])));
   __builtin_amdgcn_sched_barrier(0);
-  // o[3] is the last MFMA's accumulator: reading it waits for the pipe (0 * o adds nothing to a
-  // finite sum; a non-finite O turns the sum into NaN, which only sends the caller to its
-  // recompute path)
+  // o[3] is the last MFMA's accumulator (pair 15, or pair 7 with hv): reading it waits for the
+  // pipe (0 * o adds nothing to a finite sum; a non-finite O turns the sum into NaN, which only
+  // sends the caller to its recompute path)
   return __builtin_fmaf(o[3][15], 0.f, la) + lb;
 }
 
@@ -693,18 +717,18 @@ __device__ __forceinline__ float pv_with_probs(const char* vt, const bf16x2* p_o
 template <int D, int SM, bool VTR>
 __device__ __forceinline__ void softmax_tile_pv(const char* vt, const bf16x2* p_old, const f32x16& s0,
                                                 const f32x16& s1, float sl2, float& m, float& l, f32x16* o,
-                                                bf16x2* p_new, const OperandTable<D, VTR>& tb) {
+                                                bf16x2* p_new, const OperandTable<D, VTR>& tb, bool hv) {
   constexpr int DB = D / 32;
   if constexpr (SM == kSoftmaxRunningMax) {
     const float mnew = fmaxf(m, tile_row_max(s0, s1, sl2));
-    const float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, mnew, p_new, tb);
+    const float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, mnew, p_new, tb, hv);
     rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
     m = mnew;
     l += lt;
   } else if constexpr (SM == kSoftmaxFixedFirst) {
-    l += pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, tb);
+    l += pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, tb, hv);
   } else {
-    float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, tb);
+    float lt = pv_with_probs<D, VTR>(vt, p_old, o, s0, s1, sl2, m, p_new, tb, hv);
     if (__ballot(!(lt <= 0x1p16f))) {  // a big jump (the first tile is not run here)
       const float mnew = fmaxf(m, ceilf(tile_row_max(s0, s1, sl2)));
       rescale<DB>(o, l, __builtin_amdgcn_exp2f(m - mnew));
@@ -737,6 +761,11 @@ __device__ __forceinline__ void softmax_tile_pv(const char* vt, const bf16x2* p_
 // too: its tiles are copied with grid_v_copy and the P V operands read from
 // them with transpose reads (VtrSwz), so the gather need not write the
 // transposed copy Vct.  The output is the same bit for bit either way.
+// Cubes whose slots 32..63 are all padding (the last layer along t when
+// T % 4 is 1 or 2) cost less: the second wavefront of such a query cube only
+// copies and meets the barriers, and such a key cube gets the scores of its
+// first 32 keys and the P V MFMAs of those keys only -- the skipped MFMAs
+// would add zeros, so O and lse keep their bits.
 template <int D, bool GATED, int SM = kSoftmaxGuarded, class BLK = Cube, bool GRID_QK = false, bool GRID_V = false>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) wf_vsa_fine_fwd(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
@@ -757,9 +786,16 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
   cube_coords(g, c, ct, ch, cw);
   const long N = (long)g.T * g.H * g.W;
   const long head_row0 = (long)bh * N;
+  // Edge blocks whose slots 32..63 are all padding (VSA's cubes in the last layer along t when
+  // T % 4 is 1 or 2): the second wavefront of such a query block computes nothing -- it takes
+  // its share of the tile copies and meets the barriers -- and such a key block costs half the
+  // MFMAs.  Sliding-tile attention runs only on grids its slabs divide, so its instances leave
+  // all of this out (SKIP).
+  constexpr bool SKIP = BLK::BT > 1;
+  const bool idle = SKIP && wave == 1 && upper_half_padded<BLK>(block_at<BLK>(g, c, (uint32_t)N));
 
   bf16x8 qop[D / 16];
-  {
+  if (!idle) {
     if constexpr (GRID_QK) {  // a padded slot gets a zero row, as in the cube-ordered copy
       const int tq = slot_token<BLK>(g, ct, ch, cw, slot);
       const uint16_t* qr = qc + (head_row0 + (tq >= 0 ? tq : 0)) * D;
@@ -828,56 +864,81 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) w
       }
     }
   };
+  // S = K Q^T of the current tile; with keys 32..63 all padding (upper_half_padded) only the
+  // first score block is computed, the second stays zero and mask_keys sets it to -inf
+  auto scores = [&](bool upper_padded) __attribute__((always_inline)) {
+    if (upper_padded) mfma_run<D, NPV, NPV + NQK, 2>(vs, ks, pa, qop, oacc, s0, s1, otab);
+    else mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);
+  };
   // tile 0: scores and probabilities (its P V runs inside tile 1's softmax)
-  barrier_nofence();                                                     // K(0) visible
-  mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(0) Q^T
-  barrier_nofence();                                                     // K slot free
+  bool hprev = SKIP && upper_half_padded<BLK>(at_cur);  // keys 32..63 of the previous tile are padding
+  barrier_nofence();                            // K(0) visible
+  if (!idle) scores(hprev);                     // S = K(0) Q^T
+  barrier_nofence();                            // K slot free
   if (k > 1) {
     at_nxt = block_at<BLK>(g, plan[1], (uint32_t)N);
     copy_k(plan[1], at_nxt);
   }
-  mask_keys(at_cur);
-  softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, pa);
+  if (!idle) {
+    mask_keys(at_cur);
+    softmax_tile<DB, SM>(s0, s1, sl2, m, l, oacc, pa);
+  }
   wait_tile_copies();  // K(1) and V(0) landed
   barrier_nofence();   // K(1), V(0) visible
   // tile t >= 1.  LAST (the gated kernel's final tile, peeled off the loop so that the gate
   // registers are live only there) loads the gate rows and the coarse output for the epilogue
-  // where other tiles copy the next K cube, so their latency hides behind the softmax.
-  auto tile = [&](int t, auto last_c) __attribute__((always_inline)) {
-    constexpr bool LAST = decltype(last_c)::value;
+  // where other tiles copy the next K cube, so their latency hides behind the softmax.  EDGE
+  // instances check for half-padding key blocks; the others are for runs of tiles with none,
+  // in which hprev stays false.
+  auto tile = [&](int t, auto last_c, auto edge_c) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_c)::value, EDGE = decltype(edge_c)::value;
     cur = plan[t];
     at_cur = at_nxt;
-    mfma_run<D, NPV, NPV + NQK>(vs, ks, pa, qop, oacc, s0, s1, otab);  // S = K(t) Q^T
-    wait_tile_copies();  // V(t-1) landed
-    barrier_nofence();   // K slot free; V(t-1) visible
-    if constexpr (LAST)
-      gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
-    else if (t + 1 < k) {
+    const bool hcur = EDGE && SKIP && upper_half_padded<BLK>(at_cur);
+    if (!idle) scores(hcur);  // S = K(t) Q^T
+    wait_tile_copies();       // V(t-1) landed
+    barrier_nofence();        // K slot free; V(t-1) visible
+    if constexpr (LAST) {
+      if (!idle)
+        gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
+    } else if (t + 1 < k) {
       at_nxt = block_at<BLK>(g, plan[t + 1], (uint32_t)N);
       copy_k(plan[t + 1], at_nxt);
     }
-    mask_keys(at_cur);
-    softmax_tile_pv<D, SM, GRID_V>(vs, pa, s0, s1, sl2, m, l, oacc, pb, otab);  // O += P(t-1) V(t-1); P(t)
+    if (!idle) {  // O += P(t-1) V(t-1); P(t)
+      mask_keys(at_cur);
+      softmax_tile_pv<D, SM, GRID_V>(vs, pa, s0, s1, sl2, m, l, oacc, pb, otab, EDGE && hprev);
+    }
     wait_tile_copies();  // K(t+1) landed (or the gate rows)
     barrier_nofence();   // V slot free; K(t+1) visible
     copy_v(cur, at_cur);  // V(t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) pa[i] = pb[i];
+    hprev = hcur;
   };
+  // A plan in ascending order (as wf_vsa_topk writes it) lists the last layer's cubes, the
+  // half-padding ones, last: the tiles before the first of them run without the checks.
+  const int tend = GATED ? k - 1 : k;
+  int t = 1;
+  for (; t < tend && !hprev && !(SKIP && upper_half_padded<BLK>(at_nxt)); ++t)
+    tile(t, std::false_type(), std::false_type());
+  for (; t < tend; ++t) tile(t, std::false_type(), std::true_type());
   if constexpr (GATED) {
-    for (int t = 1; t < k - 1; ++t) tile(t, std::false_type());
-    if (k > 1) tile(k - 1, std::true_type());
-  } else {
-    for (int t = 1; t < k; ++t) tile(t, std::false_type());
+    if (k > 1) tile(k - 1, std::true_type(), std::true_type());
   }
   wait_tile_copies();  // V(k-1) landed
   barrier_nofence();   // V(k-1) visible
   if constexpr (GATED) {  // a single tile had no later tile to load them in
-    if (k == 1) gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
+    if (k == 1 && !idle)
+      gate_prefetch<D, BLK>(gp, g, ct, ch, cw, wave, lane, head_row0, gate, ocoarse + (cube_base + c) * D);
   }
-  mfma_run<D, 0, NPV>(vs, ks, pa, qop, oacc, s0, s1, otab);  // O += P(k-1) V(k-1)
+  if (!idle) {  // O += P(k-1) V(k-1)
+    if (hprev) mfma_run<D, 0, NPV / 2>(vs, ks, pa, qop, oacc, s0, s1, otab);
+    else mfma_run<D, 0, NPV>(vs, ks, pa, qop, oacc, s0, s1, otab);
+  }
   wait_tile_copies();  // the gate rows (k = 1)
   barrier_nofence();   // every wavefront is done with both slots
+  if (idle) return;    // no query row to write
   const float lt = l + __shfl_xor(l, 32);
   fine_epilogue<D, GATED, BLK>(oacc, 1.f / lt, wave == 0 ? ks : vs, j, half, g, ct, ch, cw, wave, head_row0, o, gp);
   const int tok = slot_token<BLK>(g, ct, ch, cw, slot);

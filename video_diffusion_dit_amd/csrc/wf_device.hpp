@@ -253,7 +253,8 @@ __device__ __forceinline__ void mfma_pair(int i, uint4 a, const bf16x2* p2, cons
   }
 }
 
-// Pairs [I0, I1): operands are read PF pairs ahead of the MFMA that consumes
+// Pairs I0, I0 + S, ... below I1 (S = 2 over the K Q^T pairs: score block s0
+// only): operands are read PF pairs ahead of the MFMA that consumes
 // them; each step is fenced with sched_barrier so the compiler keeps that
 // distance (it otherwise reads each operand right before its MFMA and the LDS
 // latency stalls the matrix pipe).  Scores are zeroed first if the run
@@ -269,34 +270,36 @@ __device__ __forceinline__ void mfma_prefill(uint4 (&ring)[kRing], const char* v
   for (int u = 0; u < kRingPF; ++u) ring[u] = table_operand<D, VTR>(I0 + u, vt, kt, tb);
 }
 
-template <int D, int I0, int I1, bool PREFILLED, bool VTR>
+template <int D, int I0, int I1, bool PREFILLED, bool VTR, int S = 1>
 __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
                                            f32x16* o, f32x16& s0, f32x16& s1, const OperandTable<D, VTR>& tb,
                                            uint4 (&ring)[kRing]) {
-  constexpr int PF = kRingPF, R = kRing, NP = I1 - I0;
+  constexpr int PF = kRingPF, R = kRing, NP = (I1 - I0 + S - 1) / S;
   static_assert(NP >= PF, "run shorter than the prefetch distance");
+  static_assert(S == 1 || (S == 2 && I0 >= Pairs<D>::NPV), "a strided run covers K Q^T pairs only");
+  static_assert(!PREFILLED || S == 1, "mfma_prefill reads consecutive pairs");
   if constexpr (I1 > Pairs<D>::NPV) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
   }
   if constexpr (!PREFILLED) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) ring[u] = table_operand<D, VTR>(I0 + u, vt, kt, tb);
+    for (int u = 0; u < PF; ++u) ring[u] = table_operand<D, VTR>(I0 + S * u, vt, kt, tb);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    if (i + PF < NP) ring[(i + PF) % R] = table_operand<D, VTR>(I0 + i + PF, vt, kt, tb);
-    mfma_pair<D>(I0 + i, ring[i % R], p2, qop, o, s0, s1);
+    if (i + PF < NP) ring[(i + PF) % R] = table_operand<D, VTR>(I0 + S * (i + PF), vt, kt, tb);
+    mfma_pair<D>(I0 + S * i, ring[i % R], p2, qop, o, s0, s1);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int D, int I0, int I1, bool VTR>
+template <int D, int I0, int I1, int S = 1, bool VTR>
 __device__ __forceinline__ void mfma_run(const char* vt, const char* kt, const bf16x2* p2, const bf16x8* qop,
                                            f32x16* o, f32x16& s0, f32x16& s1, const OperandTable<D, VTR>& tb) {
   uint4 ring[kRing];
-  mfma_run<D, I0, I1, false, VTR>(vt, kt, p2, qop, o, s0, s1, tb, ring);
+  mfma_run<D, I0, I1, false, VTR, S>(vt, kt, p2, qop, o, s0, s1, tb, ring);
 }
 
 // ------------------------------------------------------------- softmax tile

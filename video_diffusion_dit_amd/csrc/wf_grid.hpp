@@ -30,6 +30,16 @@ WF_HD constexpr uint32_t cube_first_token_at(int ct, int ch, int cw, int H, int 
   return block_first_token<4, 4, 4>(ct, ch, cw, H, W);
 }
 
+// Whether slots 32..63 of a BT x BH x BW block of 64 slots (slot s at (s / (BH BW), s / BW % BH,
+// s % BW)) are all padding, for a block that extends lt and lh tokens inside the grid along t and
+// h (BT or more, BH or more: whole): they are the block's second half along t (BT > 1) or, for
+// blocks one token deep, along h.  Every block holds at least one token on each axis.
+template <int BT, int BH, int BW>
+WF_HD constexpr bool second_half_padded(int lt, int lh) {
+  static_assert(BT * BH * BW == 64 && (BT > 1 ? BT % 2 : BH % 2) == 0, "64-slot blocks split along t, or along h");
+  return BT > 1 ? lt <= BT / 2 : lh <= BH / 2;
+}
+
 // First token of cube `cube` of the padded (nt, nh, nw) cube grid of a T x H x W token grid
 // (tokens in row-major (t, h, w) order); for an index outside [0, C), N, the head's end.
 WF_HD constexpr uint32_t cube_first_token(int cube, int C, int nh, int nw, int H, int W, uint32_t N) {
