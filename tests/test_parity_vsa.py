@@ -204,12 +204,15 @@ def test_vsa_fine_caller_plan_and_validation(wf, monkeypatch):
 
 
 @pytest.mark.parametrize("plan", [[6], [4], [2], [18], [6, 9], [0, 6], [6, 9, 10], [2, 9, 10], [18, 19, 21],
-                                  [0, 1, 6], [6, 7, 8], [17, 25, 26]])
+                                  [0, 1, 6], [6, 7, 8], [17, 25, 26], [18, 6], [19, 6, 21], [6, 20, 9]])
 def test_vsa_fine_edge_cube_plans(wf, plan):
     """The same caller plan for every query cube of a 9x10x11 grid (27 cubes, 19 of them edge cubes):
     each kind of edge cube (padded along t, h or w, or several) first, in the middle and last,
     and k = 1, 2, 3, so that the masked key slots of the first tile, of later tiles and of the
-    last tile are all exercised; every output row is compared with the oracle."""
+    last tile are all exercised; every output row is compared with the oracle.  Cubes 18..26 (the
+    last layer along t, one frame deep) have their second half all padding; the last three plans
+    put them before whole cubes, which an ascending plan never does, to exercise every transition
+    of the fine stage's half-tile path (the result does not depend on the order of the plan)."""
     import torch
     wl = synth.small_workload("vsa_edge_plans", 1, 2, 9, 10, 11, 128, structured=True, seed=23, topk=3)
     log(f"vsa fine, plan {plan} for every query cube, grid 9x10x11")
