@@ -89,7 +89,8 @@ size_t wf_attn_dense_workspace_bytes(int32_t B, int32_t Hh, int32_t N, int32_t D
  *   scale      finite and > 0 (1/sqrt(D) for the standard operation).
  *   workspace  device scratch of at least wf_attn_dense_workspace_bytes(),
  *              16-byte aligned; contents on entry are ignored and the call
- *              leaves it holding V transposed per head.
+ *              leaves it holding V transposed, one D x 64 tile per 64 keys
+ *              of each head.
  * The softmax keeps a running row maximum (section "Fixed-max softmax is a
  * numerical contract" of the Wan2.2 review), so any finite input yields
  * finite output.

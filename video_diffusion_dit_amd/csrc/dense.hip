@@ -12,9 +12,10 @@
 
 namespace wf {
 
-// V [BH][N][D] -> V^T [BH][D][Np] (Np = N rounded up to 64), keys in perm16
-// order inside each group of 16, zero columns for keys >= N.  One workgroup
-// per (bh, 64-key block), through an LDS tile.
+// V [BH][N][D] -> V^T tiles [BH][Np/64][D][64] (Np = N rounded up to 64): each
+// 64-key block of a head transposed into one contiguous D x 64 tile, keys in
+// perm16 order inside each group of 16, zero columns for keys >= N.  One
+// workgroup per (bh, 64-key block), through an LDS tile.
 template <int D>
 __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict__ v,
                                                       uint16_t* __restrict__ vt, int N, int Np) {
@@ -33,13 +34,13 @@ __global__ void __launch_bounds__(256) wf_transpose_v(const uint16_t* __restrict
     for (int t = 0; t < 8; ++t) tile[r * STR + c * 8 + t] = e[t];
   }
   __syncthreads();
-  uint16_t* dst = vt + (long)bh * D * Np + n0;
+  uint16_t* dst = vt + ((long)bh * Np + n0) * D;  // this block's tile
   for (int id = tid; id < D * 8; id += 256) {
     const int d = id / 8, pc = id % 8;  // output positions 8*pc .. 8*pc+7 of row d
     uint16_t e[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) e[t] = tile[perm16(pc * 8 + t) * STR + d];
-    *reinterpret_cast<uint4*>(dst + (long)d * Np + pc * 8) = *reinterpret_cast<const uint4*>(e);
+    *reinterpret_cast<uint4*>(dst + d * 64 + pc * 8) = *reinterpret_cast<const uint4*>(e);
   }
 }
 
@@ -80,7 +81,7 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int bh = item / nqt, qt = item % nqt;
   const long base = (long)bh * N;
   const uint16_t* kg = k + base * D;
-  const uint16_t* vg = vt + (long)bh * D * Np;
+  const uint16_t* vg = vt + (long)bh * D * Np;  // the head's V^T tiles, tile t at vg + t * 64 * D
   const int qrow = qt * 256 + wave * 32 + j;
 
   bf16x8 qop[D / 16];
@@ -105,13 +106,13 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int nt = (N + 63) / 64;
   // Three K slots and three V slots: tile t's K sits in slot t % 3, its V in slot t % 3.
   // Prologue: K(0), K(1) and V(0) by half A, V(1) by half B.
-  const CopyOffsets<D, 4> coff(wq, lane, Np);
-  const uint32_t vbytes = (uint32_t)D * Np * 2;  // one head's V^T
+  const CopyOffsets<D, 4> coff(wq, lane, 64);  // V^T tile rows are 64 keys apart
+  constexpr uint32_t VTB = Swz<D>::VB;           // bytes of one V^T tile
   if (!isB) {
     tile_copy<D, 4>(coff, kg, N, kt0, nullptr, 0, 0, nullptr, wq);
-    tile_copy<D, 4>(coff, nt > 1 ? kg + 64 * D : nullptr, N - 64, kt1, vg, Np, vbytes, vt0, wq);
+    tile_copy<D, 4>(coff, nt > 1 ? kg + 64 * D : nullptr, N - 64, kt1, vg, 64, VTB, vt0, wq);
   } else {
-    tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + 64, Np, nt > 1 ? vbytes - 128u : 0u, vt1, wq);
+    tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + 64 * D, 64, nt > 1 ? VTB : 0u, vt1, wq);
   }
   __syncthreads();  // its fence waits for all four copies
   if (isB) __syncthreads();  // half B runs one phase behind
@@ -147,8 +148,8 @@ wf_dense_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if constexpr (HALF_A)
       tile_copy<D, 4>(coff, kg + (long)(t + 2) * 64 * D, N - (t + 2) * 64, knext, nullptr, 0, 0u, nullptr, wq);
     else
-      tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + (long)(t + 2) * 64, Np,
-                      t + 2 < nt ? vbytes - (uint32_t)(t + 2) * 128 : 0u, const_cast<char*>(vprev), wq);
+      tile_copy<D, 4>(coff, nullptr, 0, nullptr, vg + (long)(t + 2) * 64 * D, 64, t + 2 < nt ? VTB : 0u,
+                      const_cast<char*>(vprev), wq);
     mfma_prefill<D, 0>(ring, vnext, kcur, otab);  // first operands of MFMA phase t+1: V(t) rows
     if (t < nt) {
       if ((t + 1) * 64 > N) {  // ragged last tile: keys >= N do not exist
