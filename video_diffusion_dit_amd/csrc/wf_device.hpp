@@ -120,10 +120,13 @@ __device__ __forceinline__ void tile_copy(const CopyOffsets<D, NWC>& off, const 
   typedef __attribute__((address_space(3))) void* lds_ptr;
   constexpr int KSTEP = CO::G::KSTEP;  // global bytes between pieces i and i + KPER
   if (kg) {  // one descriptor per KPER-piece step, bounded at row krows (scalar work only)
+    const int kbytes = __builtin_amdgcn_readfirstlane(krows * D * 2);  // uniform: the clamps below stay scalar
 #pragma unroll
     for (int i = 0; i < CO::KPW; ++i) {
-      const int base = (i / CO::KPER) * KSTEP, left = krows * D * 2 - base;
-      const uint32_t bytes = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : min(left, KSTEP));  // keep it scalar
+      const int base = (i / CO::KPER) * KSTEP;
+      int left = max(kbytes - base, 0);
+      asm volatile("" : "+s"(left));  // SGPR: keeps the clamp off the vector unit (no v_med3 + readfirstlane)
+      const uint32_t bytes = (uint32_t)min(left, KSTEP);
       const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(reinterpret_cast<const char*>(kg) + base, bytes);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kdst + (i * NWC + w) * 1024), 16,
                                                (int)off.k[i % CO::KPER], 0, 0, 0);
